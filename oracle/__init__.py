@@ -1,0 +1,42 @@
+"""CPU oracle for the fine-grained-scaled FP8 GEMM.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding)
+never imports, links or calls it, and shares no code with it: no kernels,
+tables, helpers or constants.  Inputs reach both sides from ``workloads/``.
+
+What it computes, written out plainly in FP64 with numpy:
+
+* an E4M3 decode table built from the format's closed form (``e4m3.py``);
+* dense ``D = C + A @ B.T`` in NT layout with per-(row, 128-K) FP32 scales on
+  A and per-128x128-block FP32 scales on B (``gemm.py``);
+* the M-grouped contiguous and masked variants as per-group dense GEMMs,
+  reporting which rows the library must leave unwritten (``gemm.py``);
+* the acceptance check (``check.py``).
+
+Sources, by page title and section:
+
+* DeepGEMM README as mirrored on the page "Weight gradient kernels for dense
+  and MoE models #95": "Interfaces > Notices" (D = C + A @ B.T, NT layout,
+  FP32 scale factors on SM90, transposed LHS scale layout), "Grouped GEMMs
+  (contiguous layout)" (M-only grouping, segments aligned to the M block),
+  "Grouped GEMMs (masked layout)" (a mask tensor; only valid parts computed).
+* GeekNews digest "DeepGEMM: बारीक scaling के जरिए साफ़ और efficient FP8 GEMM
+  kernel": section "GEMM interface और layout constraints" (same interface
+  facts) and the Hacker News comments on promotion of MMA partial sums into
+  FP32 accumulators.
+
+Every function is pinned by tests under ``tests/`` marked ``not gpu``
+(closed forms, brute force in exact rationals, one-hot products, scale
+linearity, grouped-equals-dense).  No function here is "parity unpinned".
+"""
+
+from .e4m3 import E4M3_TABLE, e4m3_closed_form, decode_e4m3  # noqa: F401
+from .gemm import (  # noqa: F401
+    dequant_a,
+    dequant_b,
+    ref_dense,
+    ref_contiguous,
+    ref_masked,
+)
+from .check import tolerance_report, assert_close, TOL_REL, TOL_RMS, TOL_COS  # noqa: F401
