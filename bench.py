@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained-scaled FP8 GEMM library on one MI355X.
+
+One step = one pass of the selected workload (default: the 15-shape dense
+sweep, M in {64, 128, 4096} x (N, K) in {(2112,7168), (24576,1536),
+(7168,16384), (4096,7168), (7168,2048)}, BF16 out) through the library's
+C ABI, with inputs already resident in HBM.  Prints ONE JSON line:
+
+  value        whole-job FP8 TFLOPS = algorithmic flops of the step / wall time
+  roofline     the dominant launch (largest per-launch time) against the MI355X
+               dense-FP8 MFMA peak (or HBM bandwidth when that binds), timed
+               with HIP events on the stream the library launches on
+  cpu_baseline the FP64 CPU oracle on a bounded sample of the same workload
+  detail       per-shape TFLOPS and roofline fractions
+
+Algorithmic work counts only what the method must do: flops 2*N*K per valid
+row; bytes = A (valid rows) + B (groups with valid rows) + scales + D (valid
+rows) (+ C).  Padding rows and masked rows are never counted.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (no sparsity)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def algorithmic_work(x: dict):
+    """(flops, bytes) the method must do for one call on inputs ``x``."""
+    import numpy as np
+    k = x["k"]
+    kb = k // 128
+    out_b = 2 if x["out_dtype"] == "bf16" else 4
+    n = x["n"]
+    nb = _cdiv(n, 128)
+    if x["kind"] == "dense":
+        m = x["m"]
+        c_b = m * n * out_b if x.get("c") is not None else 0
+        return 2.0 * m * n * k, m * k + n * k + 4 * m * kb + 4 * nb * kb + m * n * out_b + c_b
+    if x["kind"] == "contiguous":
+        sizes = np.asarray(x["m_sizes"])
+        rows = int(sizes.sum())
+        groups = int((sizes > 0).sum())
+    else:
+        sizes = np.clip(np.asarray(x["masked_m"]), 0, x["m_max"])
+        rows = int(sizes.sum())
+        groups = int((sizes > 0).sum())
+    flops = 2.0 * rows * n * k
+    byts = rows * k + groups * n * k + 4 * rows * kb + 4 * groups * nb * kb + rows * n * out_b
+    return flops, byts
+
+
+class Case:
+    """One GEMM call with its inputs uploaded to the GPU."""
+
+    def __init__(self, desc: dict, dev: str):
+        import numpy as np
+        import torch
+        import moe_grouped_gemm_tiles_amd as dg
+
+        self.label = desc["label"]
+        self.x = x = desc["gen"]()
+        self.flops, self.bytes = algorithmic_work(x)
+
+        def up(v):
+            return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+        a = up(x["a"]).view(torch.float8_e4m3fn)
+        b = up(x["b"]).view(torch.float8_e4m3fn)
+        sfa, sfb = up(x["sfa"]), up(x["sfb"])
+        dt = torch.bfloat16 if x["out_dtype"] == "bf16" else torch.float32
+        if x["kind"] == "dense":
+            d = torch.empty(x["m"], x["n"], dtype=dt, device=dev)
+            c = up(x["c"]).to(dt) if x.get("c") is not None else None
+            self.call = lambda: dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c)
+        elif x["kind"] == "contiguous":
+            d = torch.empty(x["m_total"], x["n"], dtype=dt, device=dev)
+            mi = up(x["m_indices"])
+            self.call = lambda: dg.m_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, mi)
+        else:
+            d = torch.empty(x["num_groups"], x["m_max"], x["n"], dtype=dt, device=dev)
+            mm = up(x["masked_m"])
+            em = int(x["m_max"] // 2)
+            self.call = lambda: dg.m_grouped_fp8_gemm_nt_masked((a, sfa), (b, sfb), d, mm, em)
+        self.d = d
+        rt_mfma = self.flops / (PEAK_FP8_TFLOPS * 1e12)
+        rt_hbm = self.bytes / (PEAK_HBM_GBS * 1e9)
+        self.bound = "mfma" if rt_mfma >= rt_hbm else "hbm"
+        self.roof_s = max(rt_mfma, rt_hbm)
+
+
+
+def time_launches(case: Case, iters: int, flush=None):
+    """Median per-launch time (s) with HIP events on the current stream."""
+    import torch
+    times = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        case.call()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e) * 1e-3)
+    times.sort()
+    return times[len(times) // 2]
+
+
+def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
+    """Time the FP64 oracle on a bounded sample (first rows x first columns of every case)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    total_flops, total_s = 0.0, 0.0
+    for x in inputs:
+        n, k = x["n"], x["k"]
+        cols = np.arange(min(n, budget_cols))
+        t0 = time.perf_counter()
+        if x["kind"] == "dense":
+            rows = np.arange(min(x["m"], budget_rows))
+            oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"), rows=rows, cols=cols)
+            nrows = len(rows)
+        elif x["kind"] == "contiguous":
+            valid = np.nonzero(x["m_indices"] >= 0)[0][:budget_rows]
+            oracle.ref_contiguous(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"], rows=valid, cols=cols)
+            nrows = len(valid)
+        else:
+            groups = np.arange(min(x["num_groups"], 2))
+            oracle.ref_masked(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
+            nrows = int(np.clip(x["masked_m"][groups], 0, x["m_max"]).sum())
+        total_s += time.perf_counter() - t0
+        total_flops += 2.0 * nrows * len(cols) * k
+    return dict(value=total_flops / total_s / 1e12, unit="TFLOPS", cores=int(threads), kind="oracle",
+                sample=f"first {budget_rows} valid rows x first {budget_cols} columns of every case "
+                       f"(masked: first 2 groups), FP64 numpy, {total_flops / 1e9:.1f} GFLOP in {total_s:.1f} s",
+                host_cpus=len(os.sched_getaffinity(0)))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="dense_sweep")
+    ap.add_argument("--cases", default="", help="comma-separated case indices of the workload to keep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=512, help="cache flush buffer for the per-shape cold timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this library is measured on one GPU; --gpus above 1 is not supported "
+              "(multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    descs = workload(args.workload)
+    if args.cases:
+        keep = [int(v) for v in args.cases.split(",")]
+        descs = [descs[i] for i in keep]
+    print(f"bench: generating {len(descs)} case(s) of {args.workload}", file=sys.stderr, flush=True)
+    cases = []
+    for desc in descs:
+        c = Case(desc, dev)
+        cases.append(c)
+        print(f"bench:   {c.label}: {c.flops / 1e9:.1f} GFLOP, {c.bytes / 1e6:.1f} MB, {c.bound}-bound",
+              file=sys.stderr, flush=True)
+
+    # per-launch timing, warm (back to back) and cold (after a cache flush)
+    flush_buf = torch.empty(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.fill_(1.0)
+    detail = []
+    for c in cases:
+        c.call()
+        torch.cuda.synchronize()
+        warm = time_launches(c, 10)
+        cold = time_launches(c, 10, flush)
+        c.warm_s, c.cold_s = warm, cold
+        detail.append(dict(case=c.label, bound=c.bound, tflops_cold=c.flops / cold / 1e12,
+                           tflops_warm=c.flops / warm / 1e12, us_cold=cold * 1e6, us_warm=warm * 1e6,
+                           roofline_frac_cold=c.roof_s / cold, roofline_frac_warm=c.roof_s / warm))
+        print(f"bench:   {c.label}: cold {cold * 1e6:.1f} us ({c.flops / cold / 1e12:.1f} TFLOPS, "
+              f"{100 * c.roof_s / cold:.1f}% of roofline), warm {warm * 1e6:.1f} us", file=sys.stderr, flush=True)
+    del flush_buf
+    dom = max(range(len(cases)), key=lambda i: cases[i].warm_s)
+
+    # the timed steps
+    for _ in range(args.warmup):
+        for c in cases:
+            c.call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, c in enumerate(cases):
+            if i == dom:
+                ev[s][0].record()
+                c.call()
+                ev[s][1].record()
+            else:
+                c.call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    dom_s = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / args.steps
+    step_flops = sum(c.flops for c in cases)
+    value = step_flops * args.steps / elapsed / 1e12
+
+    dc = cases[dom]
+    if dc.bound == "mfma":
+        roof = dict(bound="mfma", achieved=dc.flops / dom_s / 1e12, peak=PEAK_FP8_TFLOPS, unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=dc.bytes / dom_s / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_case"] = dc.label
+    roof["avg_launch_us"] = dom_s * 1e6
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline([c.x for c in cases])
+
+    out = {
+        "metric": "FP8 scaled-GEMM TFLOPS and % of MI355X dense-FP8 peak (dense, grouped)",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate",
+        "data": "synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 FP32 scales)",
+        "config": {"workload": args.workload, "cases": [c.label for c in cases],
+                   "out_dtype": cases[0].x["out_dtype"], "pct_of_fp8_peak": 100.0 * value / PEAK_FP8_TFLOPS},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * dg.h -- C ABI of libdg: fine-grained-scaled FP8 GEMM for AMD Instinct
+ * MI355X (gfx950, CDNA4).
+ *
+ * Computes D = C + A @ B.T in NT layout (A row-major [M,K], B row-major
+ * [N,K], i.e. both K-contiguous) where A and B hold OCP E4M3 (E4M3FN) byte
+ * codes, A carries one FP32 scale per (row, 128-wide K block) and B one FP32
+ * scale per 128x128 block.  Sources, by page title and section:
+ *
+ *   [README]  DeepGEMM README as mirrored on the page "Weight gradient
+ *             kernels for dense and MoE models #95" (English); the same text
+ *             is summarised on the GeekNews page "DeepGEMM: बारीक scaling के
+ *             जरिए साफ़ और efficient FP8 GEMM kernel".
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library keeps no pointer after the call returns.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     Nothing synchronises with the host; entry points are safe to capture
+ *     into a HIP graph once the library has run the same configuration
+ *     outside capture (see "Workspace" below).
+ *   - Scale layouts:
+ *       sfa: FP32 [K/128][ld_sfa], transposed ("MN-major"): sfa[kb*ld_sfa + m]
+ *            scales A[m, kb*128 .. kb*128+127].  ld_sfa >= rows of A and
+ *            ld_sfa % 4 == 0 (16-byte rows), see dg_get_sf_aligned_size.
+ *            ([README] "Interfaces > Notices": the LHS scale factor is FP32
+ *            on SM90-class parts and must be in a transposed, aligned layout.)
+ *       sfb: FP32 [ceil(N/128)][K/128] row-major: sfb[nb*(K/128) + kb] scales
+ *            B[nb*128 .. nb*128+127, kb*128 .. kb*128+127] (the last row
+ *            block may be partial when N % 128 != 0).
+ *   - Accumulation: each 128-K slab's FP8 product is computed on the matrix
+ *     cores, scaled by sfa*sfb and added into FP32 accumulators; C (if any)
+ *     is added in FP32 and D is rounded once (BF16: round to nearest even).
+ *   - Determinism: for a fixed shape and device CU count, repeated calls
+ *     give bit-identical D (no floating-point atomics; fixed reduction order).
+ *   - Errors: argument problems are reported synchronously before anything
+ *     is enqueued.  Data that lives on the device (group indices, masks) is
+ *     never an error: out-of-range values are clamped or skipped so that all
+ *     memory accesses stay in bounds.
+ *
+ * Workspace: some shapes (small M, few tiles) split K across workgroups.
+ * Their FP32 partial sums go to a per-device workspace that the library
+ * allocates the first time a shape needs it (hipMalloc outside the caller's
+ * stream order) and keeps until process exit.  A call that needs a larger
+ * workspace than the current one grows it; calls under graph capture must
+ * therefore be preceded by one uncaptured call of the same shape.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_SUCCESS = 0,
+  DG_ERROR_INVALID_VALUE = 1,  /* null/misaligned pointer, bad stride, negative size, bad enum */
+  DG_ERROR_NOT_SUPPORTED = 2,  /* valid but unsupported: K % 128 != 0, contiguous M % 128 != 0 */
+  DG_ERROR_LAUNCH_FAILED = 3,  /* a HIP call failed; hipGetLastError() text via dg_last_hip_error */
+  DG_ERROR_OUT_OF_MEMORY = 4   /* workspace allocation failed */
+} dg_status;
+
+typedef enum { DG_DTYPE_BF16 = 0, DG_DTYPE_FP32 = 1 } dg_dtype;
+
+/*
+ * Dense GEMM: D[M,N] = C[M,N] + A[M,K] @ B[N,K]^T.
+ *   [README] "Interfaces > Notices" (fp8_gemm_nt computes D = C + A @ B.T) and
+ *   "Normal dense GEMMs (non-grouped)".
+ *
+ * a      E4M3 bytes, row m at a + m*lda; lda >= k, lda % 16 == 0, a 16-B aligned.
+ * sfa    FP32 [k/128][ld_sfa] as above; ld_sfa >= m, ld_sfa % 4 == 0, 16-B aligned.
+ * b      E4M3 bytes, row n at b + n*ldb; ldb >= k, ldb % 16 == 0, 16-B aligned.
+ * sfb    FP32 [ceil(n/128)][k/128], 4-B aligned.
+ * c      optional (NULL = no C); same dtype as d; row stride ldc elements,
+ *        ldc >= n, rows 16-B aligned.  c may equal d (in-place accumulate);
+ *        any other overlap of c and d is undefined.
+ * d      output, dtype d_dtype, row stride ldd elements, ldd >= n, rows 16-B aligned.
+ * m,n,k  sizes; m == 0 or n == 0 -> DG_SUCCESS with nothing enqueued;
+ *        k == 0 -> D = C (or 0); k % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
+                         const void* b, int64_t ldb, const float* sfb,
+                         const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
+                         int m, int n, int k, hipStream_t stream);
+
+/*
+ * M-grouped GEMM, contiguous layout (MoE prefill / training forward):
+ *   [README] "Grouped GEMMs (contiguous layout)": only M is grouped, N and K
+ *   are shared by all groups; tokens of all experts are concatenated and each
+ *   expert segment is aligned to the M block (dg_get_mk_alignment_for_contiguous_layout).
+ *
+ * a          E4M3 [m_total, k] contiguous (row stride k).
+ * sfa        FP32 [k/128][ld_sfa], ld_sfa >= m_total, ld_sfa % 4 == 0.
+ * b          E4M3 [num_groups, n, k] contiguous.
+ * sfb        FP32 [num_groups][ceil(n/128)][k/128] contiguous.
+ * d          [m_total, n] contiguous, dtype d_dtype.
+ * m_indices  DEVICE int32 [m_total]: group of each row, -1 on padding rows.
+ *            Row r is computed with group m_indices[r]'s B.  Rows whose index
+ *            is outside [0, num_groups) are NOT written.  The group of a
+ *            128-row block is read from its first row; a block that mixes
+ *            groups breaks the layout contract (rows of other groups are
+ *            left unwritten, never out of bounds).
+ * m_total % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa,
+                                              const void* b, const float* sfb,
+                                              void* d, dg_dtype d_dtype,
+                                              const int32_t* m_indices,
+                                              int m_total, int n, int k, int num_groups,
+                                              hipStream_t stream);
+
+/*
+ * M-grouped GEMM, masked layout (MoE decode under graph capture):
+ *   [README] "Grouped GEMMs (masked layout)": the host does not know each
+ *   expert's token count; a mask tensor tells the kernel which parts are
+ *   valid and only those are computed.
+ *
+ * a          E4M3 [num_groups, m_max, k] contiguous.
+ * sfa        FP32 [num_groups][k/128][ld_sfa], ld_sfa >= m_max, ld_sfa % 4 == 0.
+ * b          E4M3 [num_groups, n, k] contiguous.
+ * sfb        FP32 [num_groups][ceil(n/128)][k/128] contiguous.
+ * d          [num_groups, m_max, n] contiguous, dtype d_dtype.
+ * masked_m   DEVICE int32 [num_groups]: valid rows of each group, clamped to
+ *            [0, m_max].  Rows at or beyond it are NOT written.
+ * expected_m host hint of the typical masked_m (<= 0: unknown); used only to
+ *            choose tile sizes, never as data.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64_t ld_sfa,
+                                          const void* b, const float* sfb,
+                                          void* d, dg_dtype d_dtype,
+                                          const int32_t* masked_m,
+                                          int num_groups, int m_max, int n, int k,
+                                          int expected_m, hipStream_t stream);
+
+/* Row alignment of expert segments in the contiguous layout (128).
+ * [README] "Utilities": get_mk_alignment_for_contiguous_layout. */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/* Leading dimension (in floats) for a transposed FP32 scale tensor with mn
+ * rows: mn rounded up to 4 (16 bytes).  Returns -1 for mn < 0.
+ * [README] "Utilities": get_tma_aligned_size. */
+int64_t dg_get_sf_aligned_size(int64_t mn);
+
+/* Cap on compute units the kernels spread over (0 = all CUs of the current
+ * device, the default; DG_NUM_CUS in the environment sets the initial value).
+ * Negative -> DG_ERROR_INVALID_VALUE.  Process-wide.
+ * [README] "Utilities": set_num_sms / get_num_sms. */
+dg_status dg_set_num_cus(int num_cus);
+int dg_get_num_cus(void);
+
+/* Static text for a status code (never NULL). */
+const char* dg_status_string(dg_status s);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char* dg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

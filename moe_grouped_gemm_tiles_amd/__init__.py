@@ -1,0 +1,234 @@
+"""Python binding of libdg (fine-grained-scaled FP8 GEMM for MI355X / gfx950).
+
+A thin ctypes layer over the C ABI in ``include/dg.h``: it checks tensor
+dtypes/devices, passes ``data_ptr()`` values and the current HIP stream, and
+raises ``RuntimeError`` with the library's status text on failure.  All
+arithmetic runs in the HIP kernels; PyTorch only provides device memory and
+the stream.  Names mirror the DeepGEMM README ("Interfaces", "Utilities")
+as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
+
+* ``fp8_gemm_nt((a, sfa), (b, sfb), d, c=None)``
+* ``m_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, m_indices)``
+* ``m_grouped_fp8_gemm_nt_masked((a, sfa), (b, sfb), d, masked_m, expected_m)``
+* ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
+  ``set_num_cus(n)`` / ``get_num_cus()``
+
+Operands follow the ``(tensor, scale)`` pair convention of the README:
+``a`` is E4M3 (``torch.float8_e4m3fn`` or ``torch.uint8`` codes) ``[M, K]``
+(masked: ``[G, M_max, K]``), ``sfa`` is FP32 ``[K/128, ld]`` transposed
+(masked: ``[G, K/128, ld]``), ``b`` is E4M3 ``[N, K]`` (grouped
+``[G, N, K]``), ``sfb`` is FP32 ``[ceil(N/128), K/128]`` (grouped
+``[G, ceil(N/128), K/128]``), ``d`` is a caller-allocated BF16 or FP32 tensor.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "fp8_gemm_nt",
+    "m_grouped_fp8_gemm_nt_contiguous",
+    "m_grouped_fp8_gemm_nt_masked",
+    "get_mk_alignment_for_contiguous_layout",
+    "get_sf_aligned_size",
+    "set_num_cus",
+    "get_num_cus",
+    "library_path",
+    "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdg.so")
+_lib = None
+
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+_STATUS = {0: "DG_SUCCESS"}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+
+_SIGNATURES = {
+    "dg_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
+                              _i32, _i32, _i32, _vp]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                                                   _i32, _i32, _i32, _i32, _vp]),
+    "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                                               _i32, _i32, _i32, _i32, _i32, _vp]),
+    "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
+    "dg_get_sf_aligned_size": (_i64, [_i64]),
+    "dg_set_num_cus": (_i32, [_i32]),
+    "dg_get_num_cus": (_i32, []),
+    "dg_status_string": (ctypes.c_char_p, [_i32]),
+    "dg_last_hip_error": (ctypes.c_char_p, []),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdg.so (built in-tree by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libdg.so not built: run `python -m moe_grouped_gemm_tiles_amd.build` "
+                          f"(expected at {_LIB_PATH})")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        msg = lib.dg_status_string(status).decode()
+        hip = lib.dg_last_hip_error().decode()
+        raise RuntimeError(msg + (f" ({hip})" if hip and status == 3 else ""))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _unit_last_stride(t: torch.Tensor) -> bool:
+    return t.numel() == 0 or t.size(-1) == 1 or t.stride(-1) == 1
+
+
+def _fp8(t: torch.Tensor, name: str):
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} must be torch.float8_e4m3fn or uint8 codes, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not _unit_last_stride(t):
+        raise ValueError(f"{name} must be K-contiguous")
+
+
+def _f32(t: torch.Tensor, name: str):
+    if t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 GPU tensor")
+    if not _unit_last_stride(t):
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+def _out(t: torch.Tensor, name: str = "d") -> int:
+    if t.dtype not in _DTYPES or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 or float32 GPU tensor")
+    if not _unit_last_stride(t):
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+    return _DTYPES[t.dtype]
+
+
+def _dense_contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, c: torch.Tensor | None = None):
+    """D = C + A @ B.T with A [M,K], B [N,K] E4M3 and FP32 fine-grained scales."""
+    lib = load_library()
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _fp8(a, "a")
+    _fp8(b, "b")
+    _f32(sfa, "sfa")
+    _f32(sfb, "sfb")
+    _dense_contig(sfb, "sfb")
+    dt = _out(d)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or d.shape != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, d {tuple(d.shape)}")
+    if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
+        raise ValueError(f"scale shapes: sfa {tuple(sfa.shape)}, sfb {tuple(sfb.shape)}")
+    c_ptr, ldc = None, 0
+    if c is not None:
+        if c.dtype != d.dtype or c.shape != d.shape or not _unit_last_stride(c) or not c.is_cuda:
+            raise ValueError("c must match d's dtype and shape")
+        c_ptr, ldc = c.data_ptr(), c.stride(0)
+    st = lib.dg_fp8_gemm_nt(a.data_ptr(), a.stride(0), sfa.data_ptr(), sfa.stride(0),
+                            b.data_ptr(), b.stride(0), sfb.data_ptr(),
+                            c_ptr, ldc, d.data_ptr(), d.stride(0), dt, m, n, k, _stream(d))
+    _check(st)
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, m_indices: torch.Tensor):
+    """Contiguous-layout M-grouped GEMM; rows whose group index is -1 are left unwritten."""
+    lib = load_library()
+    a, sfa = a_pair
+    b, sfb = b_pair
+    for t, nm in ((a, "a"), (b, "b"), (sfb, "sfb"), (d, "d"), (m_indices, "m_indices")):
+        _dense_contig(t, nm)
+    _fp8(a, "a")
+    _fp8(b, "b")
+    _f32(sfa, "sfa")
+    _f32(sfb, "sfb")
+    dt = _out(d)
+    if m_indices.dtype != torch.int32 or not m_indices.is_cuda:
+        raise TypeError("m_indices must be an int32 GPU tensor")
+    m_total, k = a.shape
+    g, n, kb_ = b.shape
+    if kb_ != k or d.shape != (m_total, n) or m_indices.shape != (m_total,):
+        raise ValueError("shape mismatch")
+    if sfa.shape[0] != k // 128 or sfb.shape != (g, (n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    st = lib.dg_m_grouped_fp8_gemm_nt_contiguous(a.data_ptr(), sfa.data_ptr(), sfa.stride(0),
+                                                 b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
+                                                 m_indices.data_ptr(), m_total, n, k, g, _stream(d))
+    _check(st)
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d: torch.Tensor, masked_m: torch.Tensor,
+                                 expected_m: int = 0):
+    """Masked-layout M-grouped GEMM; rows at or beyond masked_m[g] are left unwritten."""
+    lib = load_library()
+    a, sfa = a_pair
+    b, sfb = b_pair
+    for t, nm in ((a, "a"), (sfa, "sfa"), (b, "b"), (sfb, "sfb"), (d, "d"), (masked_m, "masked_m")):
+        _dense_contig(t, nm)
+    _fp8(a, "a")
+    _fp8(b, "b")
+    _f32(sfa, "sfa")
+    _f32(sfb, "sfb")
+    dt = _out(d)
+    if masked_m.dtype != torch.int32 or not masked_m.is_cuda:
+        raise TypeError("masked_m must be an int32 GPU tensor")
+    g, m_max, k = a.shape
+    n = b.shape[1]
+    if b.shape != (g, n, k) or d.shape != (g, m_max, n) or masked_m.shape != (g,):
+        raise ValueError("shape mismatch")
+    if sfa.dim() != 3 or sfa.shape[:2] != (g, k // 128) or sfb.shape != (g, (n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    st = lib.dg_m_grouped_fp8_gemm_nt_masked(a.data_ptr(), sfa.data_ptr(), sfa.stride(1),
+                                             b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
+                                             masked_m.data_ptr(), g, m_max, n, k, int(expected_m),
+                                             _stream(d))
+    _check(st)
+    return d
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return load_library().dg_get_mk_alignment_for_contiguous_layout()
+
+
+def get_sf_aligned_size(mn: int) -> int:
+    return load_library().dg_get_sf_aligned_size(mn)
+
+
+def set_num_cus(n: int):
+    _check(load_library().dg_set_num_cus(n))
+
+
+def get_num_cus() -> int:
+    return load_library().dg_get_num_cus()

@@ -1,0 +1,100 @@
+"""Ahead-of-time build of libdg.so for gfx950 with hipcc.
+
+``python -m moe_grouped_gemm_tiles_amd.build`` compiles the HIP sources into
+``moe_grouped_gemm_tiles_amd/libdg.so`` (in-tree).  The build asks the
+compiler for each kernel's resource usage and fails if any kernel spills to
+scratch memory (the counterpart of DeepGEMM's DG_JIT_PTXAS_CHECK switch,
+README section "Utilities", which asserts no local memory use); the usage
+table is written next to the library as ``libdg.resources.txt``.
+"""
+
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdg.so")
+RES = os.path.join(PKG, "libdg.resources.txt")
+ARCH = "gfx950"
+
+SOURCES = [os.path.join(CSRC, "dg_api.hip")]
+HEADERS = [os.path.join(CSRC, "dg_kernels.hpp"), os.path.join(INCLUDE, "dg.h")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def compile_cmd(out: str) -> list:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed FP32 instructions stay off for all device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Rpass-analysis=kernel-resource-usage",
+        "-I", INCLUDE, "-I", CSRC,
+        *SOURCES, "-o", out,
+    ]
+
+
+def _parse_resources(stderr: str):
+    kernels = []
+    cur = None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            kernels.append(cur)
+            continue
+        if cur is None:
+            continue
+        for key, pat in (("sgpr", r"SGPRs: (\d+)"), ("vgpr", r"VGPRs: (\d+)"), ("agpr", r"AGPRs: (\d+)"),
+                         ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                         ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)"),
+                         ("lds", r"LDS Size \[bytes/block\]: (\d+)")):
+            m = re.search(pat, line)
+            if m:
+                cur[key] = int(m.group(1))
+    return kernels
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = compile_cmd(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    kernels = _parse_resources(proc.stderr)
+    lines = [f"{'kernel':<90} {'vgpr':>5} {'agpr':>5} {'sgpr':>5} {'scratch':>8} {'lds':>7} {'occ':>4}"]
+    spills = []
+    for kr in kernels:
+        lines.append(f"{kr['name'][:90]:<90} {kr.get('vgpr', -1):>5} {kr.get('agpr', -1):>5} "
+                     f"{kr.get('sgpr', -1):>5} {kr.get('scratch', -1):>8} {kr.get('lds', -1):>7} "
+                     f"{kr.get('occupancy', -1):>4}")
+        if kr.get("scratch", 0) != 0:
+            spills.append(kr["name"])
+    with open(RES, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if spills:
+        os.unlink(tmp)
+        raise RuntimeError("kernels use scratch memory (register spills): " + ", ".join(spills))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("\n".join(lines))
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

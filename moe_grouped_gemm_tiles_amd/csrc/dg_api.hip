@@ -1,0 +1,270 @@
+// dg_api.hip -- host side of libdg: argument validation, tile-config choice
+// and kernel launch for the C ABI declared in include/dg.h.
+//
+// Source for the operations and their conventions: DeepGEMM README as
+// mirrored on "Weight gradient kernels for dense and MoE models #95",
+// sections "Interfaces > Notices", "Grouped GEMMs (contiguous layout)",
+// "Grouped GEMMs (masked layout)" and "Utilities" (SM cap, contiguous-layout
+// alignment, aligned scale size); the DG_PRINT_CONFIGS switch mirrors the
+// README's environment variable of the same name ("General").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "dg.h"
+#include "dg_kernels.hpp"
+
+namespace {
+
+constexpr int kAlignM = 128;
+constexpr int kMaxDevices = 64;
+
+thread_local char g_last_hip_error[256] = "";
+
+std::atomic<int> g_num_cus{-1};  // -1: not yet read from the environment
+int g_device_cus[kMaxDevices] = {0};
+std::once_flag g_env_once;
+bool g_print_configs = false;
+
+void read_env() {
+  std::call_once(g_env_once, [] {
+    const char* s = std::getenv("DG_PRINT_CONFIGS");
+    g_print_configs = s && std::atoi(s) != 0;
+    int expected = -1;
+    const char* c = std::getenv("DG_NUM_CUS");
+    const int v = c ? std::atoi(c) : 0;
+    g_num_cus.compare_exchange_strong(expected, v > 0 ? v : 0);
+  });
+}
+
+dg_status hip_fail(hipError_t e) {
+  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
+  return DG_ERROR_LAUNCH_FAILED;
+}
+
+// CUs the kernels may spread over on the current device.
+dg_status usable_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  int total = (dev >= 0 && dev < kMaxDevices) ? g_device_cus[dev] : 0;
+  if (total <= 0) {
+    e = hipDeviceGetAttribute(&total, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev >= 0 && dev < kMaxDevices) g_device_cus[dev] = total;
+  }
+  read_env();
+  const int cap = g_num_cus.load();
+  *out = (cap > 0 && cap < total) ? cap : total;
+  return DG_SUCCESS;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline int64_t dtype_size(dg_dtype t) { return t == DG_DTYPE_BF16 ? 2 : 4; }
+
+struct Cfg {
+  int bm, bn, wm, wn;
+};
+
+using KernelFn = void (*)(dg::Params);
+
+template <int BM, int BN, int WM, int WN, int MODE>
+KernelFn pick_epilogue(dg_dtype t, bool has_c) {
+  if (t == DG_DTYPE_BF16)
+    return has_c ? dg::gemm_kernel<BM, BN, WM, WN, MODE, true, true>
+                 : dg::gemm_kernel<BM, BN, WM, WN, MODE, true, false>;
+  return has_c ? dg::gemm_kernel<BM, BN, WM, WN, MODE, false, true>
+               : dg::gemm_kernel<BM, BN, WM, WN, MODE, false, false>;
+}
+
+template <int MODE>
+KernelFn pick_kernel(const Cfg& c, dg_dtype t, bool has_c) {
+  (void)c;
+  return pick_epilogue<128, 128, 2, 2, MODE>(t, has_c);
+}
+
+const char* mode_name(int mode) {
+  return mode == dg::MODE_DENSE ? "dense" : mode == dg::MODE_CONTIG ? "contiguous" : "masked";
+}
+
+template <int MODE>
+dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int groups_for_tiles,
+                 hipStream_t stream) {
+  p.tiles_m = cdiv(p.m, cfg.bm);
+  p.tiles_n = cdiv(p.n, cfg.bn);
+  p.num_tiles = p.tiles_m * p.tiles_n * groups_for_tiles;
+  if (p.num_tiles <= 0) return DG_SUCCESS;
+  int cus = 0;
+  dg_status st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  const int occupancy = 2;  // workgroups resident per CU for the 128x128 tile (64 KiB LDS each)
+  const int grid = p.num_tiles < cus * occupancy ? p.num_tiles : cus * occupancy;
+  KernelFn fn = pick_kernel<MODE>(cfg, t, has_c);
+  if (g_print_configs)
+    std::fprintf(stderr, "dg: %s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d tiles=%d grid=%d cus=%d\n",
+                 mode_name(MODE), p.m, p.n, p.k, p.num_groups, cfg.bm, cfg.bn, cfg.wm, cfg.wn,
+                 p.num_tiles, grid, cus);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(cfg.wm * cfg.wn * 64), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return DG_SUCCESS;
+}
+
+// Shared operand checks; rows = rows of A (M, M_total or M_max).
+dg_status check_common(const void* a, const float* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                       const void* d, dg_dtype t, int rows, int n, int k) {
+  if (rows < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
+  if (t != DG_DTYPE_BF16 && t != DG_DTYPE_FP32) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_NOT_SUPPORTED;
+  if (d == nullptr || !aligned(d, 16)) return DG_ERROR_INVALID_VALUE;
+  if (k > 0) {
+    if (a == nullptr || b == nullptr || sfa == nullptr || sfb == nullptr) return DG_ERROR_INVALID_VALUE;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sfa, 16) || !aligned(sfb, 4))
+      return DG_ERROR_INVALID_VALUE;
+    if (ld_sfa < rows || ld_sfa % 4 != 0) return DG_ERROR_INVALID_VALUE;
+  }
+  return DG_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
+                         int64_t ldb, const float* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
+                         dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
+  dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m, n, k);
+  if (st != DG_SUCCESS) return st;
+  const int64_t es = dtype_size(d_dtype);
+  if (k > 0 && (lda < k || ldb < k || lda % 16 != 0 || ldb % 16 != 0)) return DG_ERROR_INVALID_VALUE;
+  if (ldd < n || (ldd * es) % 16 != 0) return DG_ERROR_INVALID_VALUE;
+  if (c != nullptr && (!aligned(c, 16) || ldc < n || (ldc * es) % 16 != 0)) return DG_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return DG_SUCCESS;
+
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = c;
+  p.d = d;
+  p.grp = nullptr;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.ldd = ldd;
+  p.ld_sfa = ld_sfa;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.num_groups = 1;
+  const Cfg cfg{128, 128, 2, 2};
+  return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, 1, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                              const float* sfb, void* d, dg_dtype d_dtype,
+                                              const int32_t* m_indices, int m_total, int n, int k,
+                                              int num_groups, hipStream_t stream) {
+  if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
+  dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_total, n, k);
+  if (st != DG_SUCCESS) return st;
+  if (m_total % kAlignM != 0) return DG_ERROR_NOT_SUPPORTED;
+  if ((static_cast<int64_t>(n) * dtype_size(d_dtype)) % 16 != 0) return DG_ERROR_INVALID_VALUE;
+  if (m_total == 0 || n == 0 || num_groups == 0) return DG_SUCCESS;
+  if (m_indices == nullptr || !aligned(m_indices, 4)) return DG_ERROR_INVALID_VALUE;
+
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = nullptr;
+  p.d = d;
+  p.grp = m_indices;
+  p.lda = k;
+  p.ldb = k;
+  p.ldd = n;
+  p.ld_sfa = ld_sfa;
+  p.b_gs = static_cast<int64_t>(n) * k;
+  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * (k / 128);
+  p.m = m_total;
+  p.n = n;
+  p.k = k;
+  p.num_groups = num_groups;
+  const Cfg cfg{128, 128, 2, 2};
+  return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, 1, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                          const float* sfb, void* d, dg_dtype d_dtype, const int32_t* masked_m,
+                                          int num_groups, int m_max, int n, int k, int expected_m,
+                                          hipStream_t stream) {
+  (void)expected_m;
+  if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
+  dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_max, n, k);
+  if (st != DG_SUCCESS) return st;
+  if ((static_cast<int64_t>(n) * dtype_size(d_dtype)) % 16 != 0) return DG_ERROR_INVALID_VALUE;
+  if (m_max == 0 || n == 0 || num_groups == 0) return DG_SUCCESS;
+  if (masked_m == nullptr || !aligned(masked_m, 4)) return DG_ERROR_INVALID_VALUE;
+
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = nullptr;
+  p.d = d;
+  p.grp = masked_m;
+  p.lda = k;
+  p.ldb = k;
+  p.ldd = n;
+  p.ld_sfa = ld_sfa;
+  p.a_gs = static_cast<int64_t>(m_max) * k;
+  p.sfa_gs = static_cast<int64_t>(k / 128) * ld_sfa;
+  p.b_gs = static_cast<int64_t>(n) * k;
+  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * (k / 128);
+  p.d_gs = static_cast<int64_t>(m_max) * n;
+  p.m = m_max;
+  p.n = n;
+  p.k = k;
+  p.num_groups = num_groups;
+  const Cfg cfg{128, 128, 2, 2};
+  return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, num_groups, stream);
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return kAlignM; }
+
+int64_t dg_get_sf_aligned_size(int64_t mn) { return mn < 0 ? -1 : (mn + 3) / 4 * 4; }
+
+dg_status dg_set_num_cus(int num_cus) {
+  if (num_cus < 0) return DG_ERROR_INVALID_VALUE;
+  read_env();
+  g_num_cus.store(num_cus);
+  return DG_SUCCESS;
+}
+
+int dg_get_num_cus(void) {
+  read_env();
+  return g_num_cus.load();
+}
+
+const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_SUCCESS: return "DG_SUCCESS";
+    case DG_ERROR_INVALID_VALUE: return "DG_ERROR_INVALID_VALUE: invalid argument (pointer, alignment, stride, size or dtype)";
+    case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED: shape not supported (K % 128 != 0 or contiguous M % 128 != 0)";
+    case DG_ERROR_LAUNCH_FAILED: return "DG_ERROR_LAUNCH_FAILED: a HIP call failed";
+    case DG_ERROR_OUT_OF_MEMORY: return "DG_ERROR_OUT_OF_MEMORY: workspace allocation failed";
+  }
+  return "DG_UNKNOWN_STATUS";
+}
+
+const char* dg_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"
