@@ -40,6 +40,8 @@ def compile_cmd(out: str) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed FP32 instructions stay off for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results feed VALU promotion: keep them in VGPRs (no AGPR round trip)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Rpass-analysis=kernel-resource-usage",
         "-I", INCLUDE, "-I", CSRC,
         *SOURCES, "-o", out,
@@ -88,6 +90,7 @@ def build(verbose: bool = False) -> str:
     with open(RES, "w") as f:
         f.write("\n".join(lines) + "\n")
     if spills:
+        print("\n".join(lines), file=sys.stderr)
         os.unlink(tmp)
         raise RuntimeError("kernels use scratch memory (register spills): " + ", ".join(spills))
     os.replace(tmp, LIB)

@@ -67,10 +67,6 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline int64_t dtype_size(dg_dtype t) { return t == DG_DTYPE_BF16 ? 2 : 4; }
 
-struct Cfg {
-  int bm, bn, wm, wn;
-};
-
 using KernelFn = void (*)(dg::Params);
 
 template <int BM, int BN, int WM, int WN, int MODE>
@@ -82,9 +78,21 @@ KernelFn pick_epilogue(dg_dtype t, bool has_c) {
                : dg::gemm_kernel<BM, BN, WM, WN, MODE, false, false>;
 }
 
+// Tile configurations.  LDS per workgroup = 2 stages x (BM + BN) x 128 B (+ BM x 4 B of
+// row scales): 130 KiB for 256x256 (one workgroup per CU), 65 KiB for 128x128 (two).
+enum TileId { TILE_256x256 = 0, TILE_128x128 = 1 };
+
+struct Cfg {
+  TileId id;
+  int bm, bn, wm, wn, per_cu;
+};
+
+constexpr Cfg kCfg256{TILE_256x256, 256, 256, 2, 4, 1};
+constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2};
+
 template <int MODE>
 KernelFn pick_kernel(const Cfg& c, dg_dtype t, bool has_c) {
-  (void)c;
+  if (c.id == TILE_256x256) return pick_epilogue<256, 256, 2, 4, MODE>(t, has_c);
   return pick_epilogue<128, 128, 2, 2, MODE>(t, has_c);
 }
 
@@ -102,8 +110,8 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int grou
   int cus = 0;
   dg_status st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
-  const int occupancy = 2;  // workgroups resident per CU for the 128x128 tile (64 KiB LDS each)
-  const int grid = p.num_tiles < cus * occupancy ? p.num_tiles : cus * occupancy;
+  const int slots = cus * cfg.per_cu;
+  const int grid = p.num_tiles < slots ? p.num_tiles : slots;
   KernelFn fn = pick_kernel<MODE>(cfg, t, has_c);
   if (g_print_configs)
     std::fprintf(stderr, "dg: %s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d tiles=%d grid=%d cus=%d\n",
@@ -163,7 +171,9 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
   p.n = n;
   p.k = k;
   p.num_groups = 1;
-  const Cfg cfg{128, 128, 2, 2};
+  if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
+    return DG_ERROR_NOT_SUPPORTED;
+  const Cfg cfg = (m > 128 && n > 128) ? kCfg256 : kCfg128;
   return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, 1, stream);
 }
 
@@ -197,7 +207,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, i
   p.n = n;
   p.k = k;
   p.num_groups = num_groups;
-  const Cfg cfg{128, 128, 2, 2};
+  if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
+  const Cfg cfg = n > 128 ? kCfg256 : kCfg128;
   return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, 1, stream);
 }
 
@@ -205,7 +216,6 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
                                           const float* sfb, void* d, dg_dtype d_dtype, const int32_t* masked_m,
                                           int num_groups, int m_max, int n, int k, int expected_m,
                                           hipStream_t stream) {
-  (void)expected_m;
   if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_max, n, k);
   if (st != DG_SUCCESS) return st;
@@ -234,7 +244,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
   p.n = n;
   p.k = k;
   p.num_groups = num_groups;
-  const Cfg cfg{128, 128, 2, 2};
+  if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
+  const int em = expected_m > 0 ? expected_m : m_max;
+  const Cfg cfg = (em > 128 && n > 128) ? kCfg256 : kCfg128;
   return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, num_groups, stream);
 }
 

@@ -11,25 +11,35 @@
 //   promoted into higher-precision FP32 accumulators with FMAs that should
 //   overlap the matrix instructions.
 //
-// Design (gfx950):
-//   * One workgroup owns a BM x BN output tile and walks K in 128-wide slabs;
+// Design (gfx950; measured: FP8 MFMA ~4.0 PFLOP/s sustained, ~7 independent
+// FP32 FMAs co-issue per 16x16x128 MFMA, LDS reads ~128 B/clk/CU):
+//   * A workgroup owns a BM x BN output tile and walks K in 128-wide slabs;
 //     each slab is exactly one scale block along K.
-//   * A and B slabs are staged global -> VGPR -> LDS, double buffered (the
-//     next slab's global loads are in flight while the current slab is
-//     multiplied).  LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by
-//     (row & 7) so that both the 16-byte writes and the 16-byte fragment reads
-//     of 8 consecutive rows hit 8 different bank groups.
-//   * Each wave owns a (BM/WM) x (BN/WN) sub-tile made of 16x16 MFMA tiles.
-//     One v_mfma_f32_16x16x128_f8f6f4 covers a full 128-K slab of a 16x16
-//     tile, so the slab partial of a tile is a single instruction with a zero
-//     accumulator input.  B is passed as the MFMA's first operand and A as the
-//     second, so that a lane's four results are four consecutive columns of
-//     one output row: the row scale sfa is then one value per lane per
-//     16-row fragment and the stores are 8/16-byte vectors.
+//   * Staging: buffer_load_dwordx4 ... lds copies each slab of A and B (and
+//     the slab's BM row scales of A) straight from global memory into LDS,
+//     double buffered, so the next slab streams in while the current one is
+//     multiplied.  The buffer descriptors end at the last valid row, so rows
+//     past M or N read as zero without any bounds arithmetic.  LDS rows are
+//     128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7), which the
+//     loads realise by permuting the global addresses (a direct load writes
+//     lane i's 16 bytes at LDS offset 16*i).  Fragment reads of 8 consecutive
+//     rows then hit 8 different bank groups.
+//   * Each wave owns a TM x TN sub-tile of 16x16 MFMA tiles.  One
+//     v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K slab of a 16x16 tile,
+//     so a slab partial is a single instruction with a zero accumulator.  B is
+//     the MFMA's first operand and A the second: a lane's four results are
+//     four consecutive columns of one output row, so the row scale is one
+//     value per lane per 16-row fragment and stores are 8/16-byte vectors.
 //   * Promotion: acc += P * (sfa[row] * sfb[block]) in FP32 after every slab.
-//   * Persistent grid: blockIdx strides over the tile list; grouped variants
-//     resolve the group on device (contiguous: from the first row's group
-//     index; masked: from masked_m), so the host never synchronises.
+//     The FMAs of fragment i-1 are issued while the MFMAs of fragment i run
+//     (P is double buffered), which is how the FP32 promotion overlaps the
+//     matrix core here.
+//   * Persistent grid, XCD-aware: workgroup b runs on XCD b % 8, so tile ids
+//     are renumbered so that the workgroups of one XCD take consecutive ids,
+//     and consecutive ids form compact (GM x n) blocks of tiles that share A
+//     and B panels in that XCD's L2.
+//   * Grouped variants resolve groups on device (contiguous: group index of a
+//     tile's 128-row halves; masked: masked_m), so the host never synchronises.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +50,7 @@ namespace dg {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 
@@ -58,10 +69,23 @@ struct Params {
   int tiles_m, tiles_n, num_tiles;
 };
 
-// v_mfma_f32_16x16x128_f8f6f4 with both operands in E4M3 (format code 0) and
-// no block scaling (zero scale operands select the unscaled instruction).
-// Result lane l, element r: row (l % 16) of operand y, column 4*(l/16)+r of
-// operand x, i.e. out[x_row = 4*(l/16)+r][y_row = l%16] = sum_k x[.,k]*y[.,k].
+// Raw buffer descriptor: loads at byte offsets >= num_bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t v) {
+  return v <= 0 ? 0u : (v >= 0xffffffffll ? 0xffffffffu : (uint32_t)v);
+}
+
+// 16 bytes per lane from global (descriptor + per-lane byte offset) into LDS
+// at lds_base + 16 * lane.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, voff, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x128_f8f6f4, both operands E4M3 (format code 0), no block
+// scaling.  out[r] for lane l = sum_k x[4*(l/16)+r][k] * y[l%16][k].
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 x, i32x8 y) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
@@ -75,10 +99,24 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return u >> 16;
 }
 
-// Grouped raster: GM m-tiles at a time sweep all n-tiles, so concurrently
-// running workgroups share A and B panels in L2.
+// Two 16-byte reads of a swizzled 128-byte LDS row: logical chunks 2q and
+// 2q+1 (the lane's 32 K-bytes of the slab; A and B use the same K order).
+__device__ __forceinline__ i32x8 read_frag(const uint8_t* row_base, int sw0, int sw1) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(row_base + sw0);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(row_base + sw1);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Renumber workgroup b so that the workgroups of one XCD (b % 8) get
+// consecutive ids.
+__device__ __forceinline__ int xcd_remap(int b, int grid) {
+  if ((grid & 7) != 0) return b;
+  return (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+// Grouped raster: GM m-tiles at a time sweep the n-tiles.
+template <int GM>
 __device__ __forceinline__ void raster(int t, int tm, int tn, int& mb, int& nb) {
-  constexpr int GM = 8;
   const int per = GM * tn;
   const int grp = t / per;
   const int first = grp * GM;
@@ -90,198 +128,232 @@ __device__ __forceinline__ void raster(int t, int tm, int tn, int& mb, int& nb) 
 
 template <int BM, int BN, int WM, int WN, int MODE, bool BF16_OUT, bool HAS_C>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;  // 16-byte chunks per thread per slab
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, SFA_BYTES = BM * 4;
+  constexpr int STAGE = A_BYTES + B_BYTES + SFA_BYTES;
+  constexpr int A_LOADS = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per slab
+  constexpr int B_LOADS = B_BYTES / 1024 / NW;
+  constexpr int SFA_LANES = BM / 4;  // lanes of wave 0 that stage the slab's row scales (16 B each)
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
-  static_assert(A_CH * NT == BM * 8 && B_CH * NT == BN * 8, "slab must split evenly over threads");
+  static_assert(128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
+  static_assert(FN >= 2, "the promotion ring lags at most one 16-row fragment behind");
+  static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "loads must split evenly");
+  static_assert(SFA_LANES >= 1 && SFA_LANES <= 64 && SFA_LANES * 16 == SFA_BYTES, "sfa staging");
+  static_assert(MODE != MODE_CONTIG || BM == 128 || BM == 256, "contiguous tiles cover one or two 128-row blocks");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int KB = p.k >> 7;
   const int NBLK = (p.n + 127) >> 7;
   const int tiles_mn = p.tiles_m * p.tiles_n;
+  const int sw0 = ((2 * q4) ^ (r16 & 7)) << 4;
+  const int sw1 = ((2 * q4 + 1) ^ (r16 & 7)) << 4;
+  // direct-load lane geometry: LDS byte 16*lane of a 1 KiB block = row lane/8,
+  // physical chunk lane%8, which holds logical chunk (lane%8) ^ (lane/8).
+  const int ld_row = lane >> 3;
+  const int ld_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
 
-  for (int tile = blockIdx.x; tile < p.num_tiles; tile += gridDim.x) {
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  for (int tile = vb; tile < p.num_tiles; tile += gridDim.x) {
     int g = 0, t = tile;
     if (MODE == MODE_MASKED) {
       g = t / tiles_mn;
       t -= g * tiles_mn;
     }
     int mb, nb;
-    raster(t, p.tiles_m, p.tiles_n, mb, nb);
+    raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
     const int m0 = mb * BM, n0 = nb * BN;
 
-    int row_end = p.m;  // rows >= row_end are never stored
+    // Groups served by this tile (contiguous: one per 128-row half).
+    int row_end = p.m;
+    int g_half[2] = {0, 0};
+    int passes = 1;
     if (MODE == MODE_MASKED) {
       const int mm = min(max(p.grp[g], 0), p.m);
       if (m0 >= mm) continue;
       row_end = mm;
     } else if (MODE == MODE_CONTIG) {
-      g = p.grp[m0];
-      if (g < 0 || g >= p.num_groups) continue;
+      int g0 = p.grp[m0];
+      int g1 = (BM == 256 && m0 + 128 < p.m) ? p.grp[m0 + 128] : -1;
+      if (g0 < 0 || g0 >= p.num_groups) g0 = -1;
+      if (g1 < 0 || g1 >= p.num_groups) g1 = -1;
+      if (g0 < 0 && g1 < 0) continue;
+      if (g0 < 0) g0 = g1;
+      if (g1 < 0) g1 = g0;
+      g_half[0] = g0;
+      g_half[1] = g1;
+      passes = (g0 == g1) ? 1 : 2;
     }
 
-    const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0);
-    const float* SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)g * p.sfa_gs : 0);
-    const uint8_t* B = p.b + (MODE != MODE_DENSE ? (int64_t)g * p.b_gs : 0);
-    const float* SFB = p.sfb + (MODE != MODE_DENSE ? (int64_t)g * p.sfb_gs : 0);
+    for (int pass = 0; pass < passes; ++pass) {
+      if (MODE == MODE_CONTIG) g = g_half[pass];
+      // rows this wave computes: [m0 + wm*TM, +TM); skip waves with no live rows
+      const int wrow0 = m0 + wm * TM;
+      bool wave_live = wrow0 < row_end;
+      if (MODE == MODE_CONTIG && BM == 256) wave_live = wave_live && (g_half[(wm * TM) >> 7] == g);
 
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0) + (int64_t)m0 * p.lda;
+      const float* SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)g * p.sfa_gs : 0) + m0;
+      const uint8_t* B = p.b + (MODE != MODE_DENSE ? (int64_t)g * p.b_gs : 0) + (int64_t)n0 * p.ldb;
+      const float* SFB = p.sfb + (MODE != MODE_DENSE ? (int64_t)g * p.sfb_gs : 0);
+      const int64_t a_rows = p.m - m0, b_rows = p.n - n0;
 
-    i32x4 ra[A_CH], rb[B_CH];
-    auto gload = [&](int kb) {
+      // per-lane offsets of this wave's direct loads (fixed over K)
+      uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-        const int gm = m0 + row;
-        ra[i] = gm < p.m ? *reinterpret_cast<const i32x4*>(A + (int64_t)gm * p.lda + kb * 128 + ch * 16)
-                         : i32x4{0, 0, 0, 0};
-      }
+      for (int i = 0; i < A_LOADS; ++i)
+        a_off[i] = (uint32_t)(((wave * A_LOADS + i) * 8 + ld_row) * p.lda) + ld_chunk;
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-        const int gn = n0 + row;
-        rb[i] = gn < p.n ? *reinterpret_cast<const i32x4*>(B + (int64_t)gn * p.ldb + kb * 128 + ch * 16)
-                         : i32x4{0, 0, 0, 0};
-      }
-    };
-    auto lstore = [&](int buf) {
-      uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-        *reinterpret_cast<i32x4*>(base + row * 128 + ((ch ^ (row & 7)) << 4)) = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-        *reinterpret_cast<i32x4*>(base + BM * 128 + row * 128 + ((ch ^ (row & 7)) << 4)) = rb[i];
-      }
-    };
+      for (int i = 0; i < B_LOADS; ++i)
+        b_off[i] = (uint32_t)(((wave * B_LOADS + i) * 8 + ld_row) * p.ldb) + ld_chunk;
 
-    if (KB > 0) {
-      gload(0);
-      lstore(0);
-    }
-    __syncthreads();
+      // scale block of this wave's columns (clamped: columns past N are never stored)
+      const int sfb_blk = min((n0 + wn * TN) >> 7, NBLK - 1);
+      const float* SFB_w = SFB + (int64_t)sfb_blk * KB;
 
-    for (int kb = 0; kb < KB; ++kb) {
-      const int cur = kb & 1;
-      if (kb + 1 < KB) gload(kb + 1);
+      auto issue_slab = [&](int kb, int stage) {
+        uint8_t* base = lds + stage * STAGE;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + kb * 128, clamp_bytes(a_rows * p.lda - kb * 128));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + kb * 128, clamp_bytes(b_rows * p.ldb - kb * 128));
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) load_to_lds16(ra, base + (wave * A_LOADS + i) * 1024, a_off[i]);
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i)
+          load_to_lds16(rb, base + A_BYTES + (wave * B_LOADS + i) * 1024, b_off[i]);
+        if (wave == 0 && lane < SFA_LANES) {
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA + (int64_t)kb * p.ld_sfa, clamp_bytes(a_rows * 4));
+          load_to_lds16(rs, base + A_BYTES + B_BYTES, lane * 16);
+        }
+      };
 
-      float sa[FM], sb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int gm = m0 + wm * TM + i * 16 + r16;
-        sa[i] = gm < p.m ? SFA[(int64_t)kb * p.ld_sfa + gm] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int bn = (n0 + wn * TN + j * 16) >> 7;
-        sb[j] = bn < NBLK ? SFB[(int64_t)bn * KB + kb] : 0.f;
-      }
-
-      const uint8_t* As = lds + cur * STAGE;
-      const uint8_t* Bs = As + BM * 128;
-      const int sw0 = ((2 * q4) ^ (r16 & 7)) << 4;
-      const int sw1 = ((2 * q4 + 1) ^ (r16 & 7)) << 4;
-      i32x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint8_t* rowp = As + (wm * TM + i * 16 + r16) * 128;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + sw0);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + sw1);
-        fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint8_t* rowp = Bs + (wn * TN + j * 16 + r16) * 128;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + sw0);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + sw1);
-        fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      f32x4 acc[FM][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const f32x4 part = mfma_fp8_16x16x128(fb[j], fa[i]);
-          const float s = sa[i] * sb[j];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s, acc[i][j][r]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      if (KB > 0) issue_slab(0, 0);
+      float sb_next = KB > 0 ? SFB_w[0] : 0.f;
+
+      for (int kb = 0; kb < KB; ++kb) {
+        const int cur = kb & 1;
+        const float sb = sb_next;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of slab kb have landed
+        __syncthreads();                // ... and everyone's; stage cur^1 is free
+        if (kb + 1 < KB) {
+          issue_slab(kb + 1, cur ^ 1);
+          sb_next = SFB_w[kb + 1];
         }
-
-      if (kb + 1 < KB) lstore(cur ^ 1);
-      __syncthreads();
-    }
-
-    // Epilogue: D = C + acc, masked stores.
+        if (wave_live) {
+          const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
+          const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
+          const float* Ss = reinterpret_cast<const float*>(lds + cur * STAGE + A_BYTES + B_BYTES) + wm * TM + r16;
+          i32x8 fb[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int gm = m0 + wm * TM + i * 16 + r16;
-      bool row_ok = gm < row_end;
-      if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
-      if (!row_ok) continue;
-      const int64_t drow = (MODE == MODE_MASKED ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+          for (int j = 0; j < FN; ++j) fb[j] = read_frag(Bs + j * 16 * 128, sw0, sw1);
+          // Flat sequence of the FM*FN MFMAs of this slab.  The partial of MFMA
+          // t is promoted right after MFMA t+2 is issued (3-deep ring), so the
+          // promotion FMAs run under the matrix core.
+          constexpr int T = FM * FN;
+          constexpr int RING = 3;
+          f32x4 part[RING];
+          float s_cur = Ss[0] * sb, s_prev = 0.f;
+          i32x8 fa = read_frag(As, sw0, sw1);
+          i32x8 fa_next = fa;
+          float s_next = s_cur;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int gn = n0 + wn * TN + j * 16 + 4 * q4;
-        if (gn >= p.n) continue;
-        f32x4 v = acc[i][j];
-        const bool full = gn + 4 <= p.n;
-        if (HAS_C) {
-          const int64_t crow = (int64_t)gm * p.ldc;
-          if (BF16_OUT) {
-            const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (full || gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
-          } else {
-            const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
-            if (full) {
-              const f32x4 cv = *reinterpret_cast<const f32x4*>(C);
-              v += cv;
-            } else {
+          for (int t = 0; t < T + RING - 1; ++t) {
+            const int i = t / FN, j = t % FN;
+            if (t < T) {
+              if (j == 0 && i + 1 < FM) {
+                fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
+                s_next = Ss[(i + 1) * 16] * sb;
+              }
+              part[t % RING] = mfma_fp8_16x16x128(fb[j], fa);
+            }
+            const int u = t - (RING - 1);  // MFMA whose partial is promoted now
+            if (u >= 0) {
+              const int ui = u / FN, uj = u % FN;
+              // s_cur is fragment i's scale, s_prev fragment i-1's (u is at most one fragment behind t)
+              const float su = (t >= T || ui == i) ? s_cur : s_prev;
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (gn + r < p.n) v[r] += C[r];
+                acc[ui][uj][r] = __builtin_fmaf(part[u % RING][r], su, acc[ui][uj][r]);
+            }
+            if (t < T && j == FN - 1 && i + 1 < FM) {
+              fa = fa_next;
+              s_prev = s_cur;
+              s_cur = s_next;
             }
           }
         }
-        if (BF16_OUT) {
-          uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
-          if (full) {
-            const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-            const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(D) = make_uint2(lo, hi);
-          } else {
+      }
+      __syncthreads();  // all LDS reads of this tile are done before the next tile's loads
+
+      if (!wave_live) continue;
+      // Epilogue: D = C + acc, masked stores.
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (gn + r < p.n) D[r] = (uint16_t)bf16_rne_bits(v[r]);
+      for (int i = 0; i < FM; ++i) {
+        const int gm = wrow0 + i * 16 + r16;
+        bool row_ok = gm < row_end;
+        if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
+        if (!row_ok) continue;
+        const int64_t drow = (MODE == MODE_MASKED ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+          if (gn >= p.n) continue;
+          f32x4 v = acc[i][j];
+          const bool full = gn + 4 <= p.n;
+          if (HAS_C) {
+            const int64_t crow = (int64_t)gm * p.ldc;
+            if (BF16_OUT) {
+              const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (full || gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
+            } else {
+              const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
+              if (full) {
+                v += *reinterpret_cast<const f32x4*>(C);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (gn + r < p.n) v[r] += C[r];
+              }
+            }
           }
-        } else {
-          float* D = reinterpret_cast<float*>(p.d) + drow + gn;
-          if (full) {
-            *reinterpret_cast<f32x4*>(D) = v;
-          } else {
+          if (BF16_OUT) {
+            uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
+            if (full) {
+              const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+              const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+              *reinterpret_cast<uint2*>(D) = make_uint2(lo, hi);
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (gn + r < p.n) D[r] = v[r];
+              for (int r = 0; r < 4; ++r)
+                if (gn + r < p.n) D[r] = (uint16_t)bf16_rne_bits(v[r]);
+            }
+          } else {
+            float* D = reinterpret_cast<float*>(p.d) + drow + gn;
+            if (full) {
+              *reinterpret_cast<f32x4*>(D) = v;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (gn + r < p.n) D[r] = v[r];
+            }
           }
         }
       }
     }
-    __syncthreads();  // LDS of this tile is free before the next tile's first stores
   }
 }
 
