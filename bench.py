@@ -164,6 +164,7 @@ def main():
     ap.add_argument("--cases", default="", help="comma-separated case indices of the workload to keep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=512, help="cache flush buffer for the per-shape cold timing")
+    ap.add_argument("--timing-iters", type=int, default=10, help="launches per shape for the warm/cold timing")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -195,8 +196,8 @@ def main():
     for c in cases:
         c.call()
         torch.cuda.synchronize()
-        warm = time_launches(c, 10)
-        cold = time_launches(c, 10, flush)
+        warm = time_launches(c, args.timing_iters)
+        cold = time_launches(c, args.timing_iters, flush)
         c.warm_s, c.cold_s = warm, cold
         detail.append(dict(case=c.label, bound=c.bound, tflops_cold=c.flops / cold / 1e12,
                            tflops_warm=c.flops / warm / 1e12, us_cold=cold * 1e6, us_warm=warm * 1e6,

@@ -22,8 +22,10 @@
 //     past M or N read as zero without any bounds arithmetic.  LDS rows are
 //     128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7), which the
 //     loads realise by permuting the global addresses (a direct load writes
-//     lane i's 16 bytes at LDS offset 16*i).  Fragment reads of 8 consecutive
-//     rows then hit 8 different bank groups.
+//     lane i's 16 bytes at LDS offset 16*i).  The 16 lanes of one fragment row
+//     group read K chunks q and q+4 (q = lane / 16), which together with the
+//     swizzle is free of bank conflicts (measured with SQ_LDS_BANK_CONFLICT;
+//     the more obvious chunks 2q, 2q+1 conflict 2-way on gfx950).
 //   * Each wave owns a TM x TN sub-tile of 16x16 MFMA tiles.  One
 //     v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K slab of a 16x16 tile,
 //     so a slab partial is a single instruction with a zero accumulator.  B is
@@ -99,8 +101,8 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return u >> 16;
 }
 
-// Two 16-byte reads of a swizzled 128-byte LDS row: logical chunks 2q and
-// 2q+1 (the lane's 32 K-bytes of the slab; A and B use the same K order).
+// Two 16-byte reads of a swizzled 128-byte LDS row: the lane's 32 K-bytes of
+// the slab (A and B use the same K order, so the order itself is free).
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* row_base, int sw0, int sw1) {
   const i32x4 lo = *reinterpret_cast<const i32x4*>(row_base + sw0);
   const i32x4 hi = *reinterpret_cast<const i32x4*>(row_base + sw1);
@@ -153,8 +155,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   const int KB = p.k >> 7;
   const int NBLK = (p.n + 127) >> 7;
   const int tiles_mn = p.tiles_m * p.tiles_n;
-  const int sw0 = ((2 * q4) ^ (r16 & 7)) << 4;
-  const int sw1 = ((2 * q4 + 1) ^ (r16 & 7)) << 4;
+  // lane group q reads logical K chunks q and q + 4 (measured free of LDS bank
+  // conflicts on gfx950 together with the (row & 7) swizzle; chunks 2q, 2q+1 are 2-way)
+  const int sw0 = (q4 ^ (r16 & 7)) << 4;
+  const int sw1 = ((q4 + 4) ^ (r16 & 7)) << 4;
   // direct-load lane geometry: LDS byte 16*lane of a 1 KiB block = row lane/8,
   // physical chunk lane%8, which holds logical chunk (lane%8) ^ (lane/8).
   const int ld_row = lane >> 3;
