@@ -32,6 +32,96 @@ if ROOT not in sys.path:
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (no sparsity)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_tiles_amd", "csrc", f) for f in ("dg_kernels.hpp", "dg_api.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_CAL_MB = 256  # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def lookup_traffic(case_label: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel source, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None  # kernel changed since the counters were taken
+    ent = rec.get("cases", {}).get(case_label)
+    return None if ent is None else ent.get("traffic_bytes")
+
+
+def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str):
+    """Summarise rocprofv3 output (trace/, fetch/, write/ under prof_dir) into a short text file and
+    record the calibrated HBM traffic of the GEMM kernel in profiles/traffic.json."""
+    import csv
+    import glob
+
+    def rows(sub, pat):
+        files = glob.glob(os.path.join(prof_dir, sub, "**", pat), recursive=True)
+        return [r for f in files for r in csv.DictReader(open(f))]
+
+    stats = rows("trace", "*kernel_stats.csv")
+    counters = {}
+    for sub, name in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        per = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            if r["Counter_Name"] == name:
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[name] = per
+
+    def mean_of(per, pred):
+        vals = [v for k, vs in per.items() if pred(k) for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    is_gemm = lambda k: "gemm_kernel" in k
+    is_copy = lambda k: "copy" in k.lower() and "gemm" not in k
+    cal_bytes = COPY_CAL_MB * (1 << 20)
+    f_gemm = mean_of(counters["FETCH_SIZE"], is_gemm)
+    w_gemm = mean_of(counters["WRITE_SIZE"], is_gemm)
+    f_copy = mean_of(counters["FETCH_SIZE"], is_copy)
+    w_copy = mean_of(counters["WRITE_SIZE"], is_copy)
+    lines = [f"# rocprofv3 summary: {case_label}", "", "Command (run from the repository root):", "", "```",
+             command, "```", "", "## Kernel trace (--kernel-trace --stats)", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    traffic = None
+    lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", ""]
+    if None not in (f_gemm, w_gemm, f_copy, w_copy):
+        kf = f_copy * 1024 / cal_bytes
+        kw = w_copy * 1024 / cal_bytes
+        traffic = f_gemm * 1024 / kf + w_gemm * 1024 / kw
+        lines += [f"- copy calibration ({COPY_CAL_MB} MiB device copy): FETCH_SIZE {f_copy:.0f} KiB "
+                  f"(factor {kf:.3f}), WRITE_SIZE {w_copy:.0f} KiB (factor {kw:.3f})",
+                  f"- GEMM kernel: FETCH_SIZE {f_gemm:.0f} KiB, WRITE_SIZE {w_gemm:.0f} KiB per dispatch",
+                  f"- calibrated HBM traffic per launch: {traffic / 1e6:.1f} MB"]
+        rec = {}
+        try:
+            rec = json.load(open(TRAFFIC_FILE))
+        except (OSError, ValueError):
+            pass
+        if rec.get("source_hash") != kernel_source_hash():
+            rec = {"source_hash": kernel_source_hash(), "cases": {}}
+        rec["cases"][case_label] = {"traffic_bytes": traffic, "fetch_kib": f_gemm, "write_kib": w_gemm,
+                                    "fetch_factor": kf, "write_factor": kw}
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+    else:
+        lines.append("- counters missing")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _cdiv(a, b):
@@ -165,7 +255,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=512, help="cache flush buffer for the per-shape cold timing")
     ap.add_argument("--timing-iters", type=int, default=10, help="launches per shape for the warm/cold timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"run one {COPY_CAL_MB} MiB device copy first (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--profile-summary", nargs=3, metavar=("PROF_DIR", "OUT_MD", "CASE_LABEL"),
+                    help="summarise rocprofv3 output collected for CASE_LABEL and exit (no GPU needed)")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the profile summary")
     args = ap.parse_args()
+
+    if args.profile_summary:
+        profile_summary(*args.profile_summary, command=args.profile_command)
+        return
 
     if args.gpus != 1:
         print("bench.py: this library is measured on one GPU; --gpus above 1 is not supported "
@@ -177,6 +276,12 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(COPY_CAL_MB * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     descs = workload(args.workload)
     if args.cases:
         keep = [int(v) for v in args.cases.split(",")]
@@ -235,7 +340,7 @@ def main():
     else:
         roof = dict(bound="hbm", achieved=dc.bytes / dom_s / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = lookup_traffic(dc.label)
     roof["kernel_case"] = dc.label
     roof["avg_launch_us"] = dom_s * 1e6
 
