@@ -10,10 +10,13 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "dg.h"
 #include "dg_kernels.hpp"
@@ -69,35 +72,110 @@ inline int64_t dtype_size(dg_dtype t) { return t == DG_DTYPE_BF16 ? 2 : 4; }
 
 using KernelFn = void (*)(dg::Params);
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int ST, int MODE>
 KernelFn pick_epilogue(dg_dtype t, bool has_c) {
   if (t == DG_DTYPE_BF16)
-    return has_c ? dg::gemm_kernel<BM, BN, WM, WN, MODE, true, true>
-                 : dg::gemm_kernel<BM, BN, WM, WN, MODE, true, false>;
-  return has_c ? dg::gemm_kernel<BM, BN, WM, WN, MODE, false, true>
-               : dg::gemm_kernel<BM, BN, WM, WN, MODE, false, false>;
+    return has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, true>
+                 : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false>;
+  return has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true>
+               : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false>;
 }
 
-// Tile configurations.  LDS per workgroup = 2 stages x (BM + BN) x 128 B (+ BM x 4 B of
-// row scales): 130 KiB for 256x256 (one workgroup per CU), 65 KiB for 128x128 (two).
-enum TileId { TILE_256x256 = 0, TILE_128x128 = 1 };
+KernelFn pick_reduce(dg_dtype t, bool has_c) {
+  if (t == DG_DTYPE_BF16) return has_c ? dg::splitk_reduce_kernel<true, true> : dg::splitk_reduce_kernel<true, false>;
+  return has_c ? dg::splitk_reduce_kernel<false, true> : dg::splitk_reduce_kernel<false, false>;
+}
+
+// Tile configurations.  LDS per workgroup = stages x ((BM + BN) x 128 B + BM x 4 B):
+//   256x256, 8 waves, 2 stages: 130 KiB (one workgroup per CU) -- large M and N
+//   128x128, 4 waves, 2 stages:  65 KiB (two per CU)           -- small grouped tiles
+//   128x128, 4 waves, 4 stages: 130 KiB, split-K              -- dense 64 < M <= 128
+//    64x128, 4 waves, 4 stages:  97 KiB, split-K              -- dense M <= 64
+// The split-K configurations stream B from HBM with three slabs in flight.
+enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x128 = 2, TILE_SK_64x128 = 3 };
 
 struct Cfg {
   TileId id;
-  int bm, bn, wm, wn, per_cu;
+  int bm, bn, wm, wn, stages, per_cu;
 };
 
-constexpr Cfg kCfg256{TILE_256x256, 256, 256, 2, 4, 1};
-constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2};
+constexpr Cfg kCfg256{TILE_256x256, 256, 256, 2, 4, 2, 1};
+constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
+constexpr Cfg kCfgSk128{TILE_SK_128x128, 128, 128, 2, 2, 4, 1};
+constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 4, 1};
 
 template <int MODE>
-KernelFn pick_kernel(const Cfg& c, dg_dtype t, bool has_c) {
-  if (c.id == TILE_256x256) return pick_epilogue<256, 256, 2, 4, MODE>(t, has_c);
-  return pick_epilogue<128, 128, 2, 2, MODE>(t, has_c);
+KernelFn pick_kernel(const Cfg& c, bool split, dg_dtype t, bool has_c) {
+  if constexpr (MODE == dg::MODE_DENSE) {
+    if (c.id == TILE_SK_128x128)
+      return split ? dg::gemm_kernel<128, 128, 2, 2, 4, MODE, true, false, false> : pick_epilogue<128, 128, 2, 2, 4, MODE>(t, has_c);
+    if (c.id == TILE_SK_64x128)
+      return split ? dg::gemm_kernel<64, 128, 1, 4, 4, MODE, true, false, false> : pick_epilogue<64, 128, 1, 4, 4, MODE>(t, has_c);
+  }
+  (void)split;
+  if (c.id == TILE_256x256) return pick_epilogue<256, 256, 2, 4, 2, MODE>(t, has_c);
+  return pick_epilogue<128, 128, 2, 2, 2, MODE>(t, has_c);
 }
 
 const char* mode_name(int mode) {
   return mode == dg::MODE_DENSE ? "dense" : mode == dg::MODE_CONTIG ? "contiguous" : "masked";
+}
+
+// ---- split-K workspace: one growable FP32 buffer per (device, stream) --------
+// Kernels on one stream run in order, so one buffer per stream is race-free.
+// Growing it synchronises that stream before freeing the old buffer; this is
+// the only allocation the library makes and it happens outside the kernels.
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, std::pair<void*, size_t>> g_ws;
+
+dg_status get_workspace(size_t bytes, hipStream_t stream, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto& ent = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
+  if (ent.second < bytes) {
+    if (ent.first != nullptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipFree(ent.first);
+      if (e != hipSuccess) return hip_fail(e);
+      ent = {nullptr, 0};
+    }
+    const size_t want = bytes + bytes / 2;
+    void* ptr = nullptr;
+    e = hipMalloc(&ptr, want);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return DG_ERROR_OUT_OF_MEMORY;
+    }
+    ent = {ptr, want};
+  }
+  *out = static_cast<float*>(ent.first);
+  return DG_SUCCESS;
+}
+
+// Split count for a skinny dense GEMM: minimise (workgroup rounds x slabs per
+// split), lightly penalising every extra split (its FP32 partial costs
+// traffic), with at least 4 slabs per split.
+int choose_splits(int tiles, int kb, int slots, int* slabs_per_split) {
+  int best_s = 1, best_sps = kb;
+  double best_cost = 1e300;
+  const int max_s = kb / 4 > 1 ? kb / 4 : 1;
+  for (int s = 1; s <= max_s; ++s) {
+    const int sps = cdiv(kb, s);
+    const int s_eff = cdiv(kb, sps);
+    const int units = tiles * s_eff;
+    const int rounds = cdiv(units, slots);
+    const double cost = static_cast<double>(rounds) * sps * (1.0 + 0.03 * (s_eff - 1));
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best_s = s_eff;
+      best_sps = sps;
+    }
+  }
+  *slabs_per_split = best_sps;
+  return best_s;
 }
 
 template <int MODE>
@@ -105,21 +183,48 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int grou
                  hipStream_t stream) {
   p.tiles_m = cdiv(p.m, cfg.bm);
   p.tiles_n = cdiv(p.n, cfg.bn);
-  p.num_tiles = p.tiles_m * p.tiles_n * groups_for_tiles;
-  if (p.num_tiles <= 0) return DG_SUCCESS;
+  p.splits = 1;
+  p.slabs_per_split = p.k / 128;
+  p.ws = nullptr;
+  p.ldw = 0;
   int cus = 0;
   dg_status st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
   const int slots = cus * cfg.per_cu;
+  bool split = false;
+  if (MODE == dg::MODE_DENSE && (cfg.id == TILE_SK_128x128 || cfg.id == TILE_SK_64x128) && p.k >= 128 * 8) {
+    int sps = 0;
+    const int s = choose_splits(p.tiles_m * p.tiles_n, p.k / 128, slots, &sps);
+    if (s > 1) {
+      split = true;
+      p.splits = s;
+      p.slabs_per_split = sps;
+      p.ldw = (p.n + 3) / 4 * 4;
+      st = get_workspace(static_cast<size_t>(s) * p.m * p.ldw * sizeof(float), stream, &p.ws);
+      if (st != DG_SUCCESS) return st;
+    }
+  }
+  p.num_tiles = p.tiles_m * p.tiles_n * groups_for_tiles * p.splits;
+  if (p.num_tiles <= 0) return DG_SUCCESS;
   const int grid = p.num_tiles < slots ? p.num_tiles : slots;
-  KernelFn fn = pick_kernel<MODE>(cfg, t, has_c);
+  KernelFn fn = pick_kernel<MODE>(cfg, split, t, has_c);
   if (g_print_configs)
-    std::fprintf(stderr, "dg: %s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d tiles=%d grid=%d cus=%d\n",
-                 mode_name(MODE), p.m, p.n, p.k, p.num_groups, cfg.bm, cfg.bn, cfg.wm, cfg.wn,
-                 p.num_tiles, grid, cus);
+    std::fprintf(stderr,
+                 "dg: %s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d stages=%d splits=%d (x%d slabs) "
+                 "tiles=%d grid=%d cus=%d\n",
+                 mode_name(MODE), p.m, p.n, p.k, p.num_groups, cfg.bm, cfg.bn, cfg.wm, cfg.wn, cfg.stages, p.splits,
+                 p.slabs_per_split, p.num_tiles, grid, cus);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(cfg.wm * cfg.wn * 64), 0, stream, p);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
+  if (split) {
+    const int64_t vecs = static_cast<int64_t>(p.m) * ((p.n + 3) / 4);
+    const int64_t want = (vecs + 255) / 256;
+    const int rgrid = static_cast<int>(want < cus * 8 ? want : cus * 8);
+    hipLaunchKernelGGL(pick_reduce(t, has_c), dim3(rgrid), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return DG_SUCCESS;
 }
 
@@ -173,7 +278,7 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
   p.num_groups = 1;
   if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
     return DG_ERROR_NOT_SUPPORTED;
-  const Cfg cfg = (m > 128 && n > 128) ? kCfg256 : kCfg128;
+  const Cfg cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? kCfg256 : kCfg128);
   return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, 1, stream);
 }
 

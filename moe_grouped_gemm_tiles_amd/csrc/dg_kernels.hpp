@@ -69,7 +69,45 @@ struct Params {
   int64_t a_gs, sfa_gs, b_gs, sfb_gs, d_gs;  // per-group strides
   int m, n, k, num_groups;
   int tiles_m, tiles_n, num_tiles;
+  // split-K (dense only): K slabs are divided into `splits` ranges of
+  // `slabs_per_split`; each range writes an FP32 partial tile to
+  // ws[split][m][n] (row stride ldw floats) and a second kernel reduces them.
+  int splits, slabs_per_split;
+  float* ws;
+  int64_t ldw;
 };
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `pending` slabs of loads (of `per` instructions each) are
+// still outstanding; `pending` is a runtime value in [0, MAXP].
+template <int MAXP, int PER>
+__device__ __forceinline__ void wait_slabs_pending(int pending) {
+  if constexpr (MAXP <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (pending >= MAXP) {
+      wait_vmcnt<MAXP * PER>();
+    } else {
+      wait_slabs_pending<MAXP - 1, PER>(pending);
+    }
+  }
+}
+
+// Uniform (scalar-cache) load of one float: the address is made wave-uniform
+// so the compiler emits s_load_dword, which is counted by lgkmcnt, not vmcnt.
+__device__ __forceinline__ float load_uniform_f32(const float* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *reinterpret_cast<const float*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 // Raw buffer descriptor: loads at byte offsets >= num_bytes return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
@@ -128,7 +166,53 @@ __device__ __forceinline__ void raster(int t, int tm, int tn, int& mb, int& nb) 
   nb = r / gsz;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool BF16_OUT, bool HAS_C>
+// D[gm][gn .. gn+3] = C + v (FP32 add, one rounding), columns past N dropped.
+// drow = element offset of row gm in D.
+template <bool BF16_OUT, bool HAS_C>
+__device__ __forceinline__ void store_out(const Params& p, int gm, int gn, int64_t drow, f32x4 v) {
+  const bool full = gn + 4 <= p.n;
+  if (HAS_C) {
+    const int64_t crow = (int64_t)gm * p.ldc;
+    if (BF16_OUT) {
+      const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (full || gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
+    } else {
+      const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
+      if (full) {
+        v += *reinterpret_cast<const f32x4*>(C);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (gn + r < p.n) v[r] += C[r];
+      }
+    }
+  }
+  if (BF16_OUT) {
+    uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
+    if (full) {
+      const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+      const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+      *reinterpret_cast<uint2*>(D) = make_uint2(lo, hi);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (gn + r < p.n) D[r] = (uint16_t)bf16_rne_bits(v[r]);
+    }
+  } else {
+    float* D = reinterpret_cast<float*>(p.d) + drow + gn;
+    if (full) {
+      *reinterpret_cast<f32x4*>(D) = v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (gn + r < p.n) D[r] = v[r];
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE, bool SPLIT, bool BF16_OUT, bool HAS_C>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -144,8 +228,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "loads must split evenly");
   static_assert(SFA_LANES >= 1 && SFA_LANES <= 64 && SFA_LANES * 16 == SFA_BYTES, "sfa staging");
   static_assert(MODE != MODE_CONTIG || BM == 128 || BM == 256, "contiguous tiles cover one or two 128-row blocks");
+  static_assert(!SPLIT || MODE == MODE_DENSE, "split-K is for dense GEMMs");
+  static_assert(STAGES >= 2, "at least double buffering");
+  // Per-wave load instructions per slab (wave 0 issues one more, for the row
+  // scales; using the smaller count makes wave 0 wait slightly longer).
+  constexpr int LOADS_PER_SLAB = A_LOADS + B_LOADS;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,11 +255,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   for (int tile = vb; tile < p.num_tiles; tile += gridDim.x) {
-    int g = 0, t = tile;
+    int g = 0, t = tile, split = 0;
     if (MODE == MODE_MASKED) {
       g = t / tiles_mn;
       t -= g * tiles_mn;
     }
+    if (SPLIT) {
+      split = t / tiles_mn;
+      t -= split * tiles_mn;
+    }
+    const int kb_begin = SPLIT ? split * p.slabs_per_split : 0;
+    const int kb_end = SPLIT ? min(KB, kb_begin + p.slabs_per_split) : KB;
+    const int nkb = kb_end - kb_begin;
     int mb, nb;
     raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
     const int m0 = mb * BM, n0 = nb * BN;
@@ -243,18 +339,20 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      if (KB > 0) issue_slab(0, 0);
-      float sb_next = KB > 0 ? SFB_w[0] : 0.f;
+      // prologue: STAGES-1 slabs in flight
+#pragma unroll
+      for (int i = 0; i < STAGES - 1; ++i)
+        if (i < nkb) issue_slab(kb_begin + i, i);
+      float sb_next = nkb > 0 ? load_uniform_f32(SFB_w + kb_begin) : 0.f;
 
-      for (int kb = 0; kb < KB; ++kb) {
-        const int cur = kb & 1;
+      for (int it = 0; it < nkb; ++it) {
+        const int cur = it % STAGES;
         const float sb = sb_next;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of slab kb have landed
-        __syncthreads();                // ... and everyone's; stage cur^1 is free
-        if (kb + 1 < KB) {
-          issue_slab(kb + 1, cur ^ 1);
-          sb_next = SFB_w[kb + 1];
-        }
+        // slabs issued after slab `it` that may stay in flight
+        wait_slabs_pending<STAGES - 2, LOADS_PER_SLAB>(min(STAGES - 2, nkb - 1 - it));
+        __syncthreads();  // slab `it` has landed for every wave; stage (it-1) % STAGES is free
+        if (it + STAGES - 1 < nkb) issue_slab(kb_begin + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+        if (it + 1 < nkb) sb_next = load_uniform_f32(SFB_w + kb_begin + it + 1);
         if (wave_live) {
           const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
           const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
@@ -302,6 +400,21 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       __syncthreads();  // all LDS reads of this tile are done before the next tile's loads
 
       if (!wave_live) continue;
+      if (SPLIT) {
+        // FP32 partial of this K range; the reduce kernel adds the ranges in order.
+        float* W = p.ws + (int64_t)split * p.m * p.ldw;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int gm = wrow0 + i * 16 + r16;
+          if (gm >= p.m) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+            if (gn < p.n) *reinterpret_cast<f32x4*>(W + (int64_t)gm * p.ldw + gn) = acc[i][j];
+          }
+        }
+        continue;
+      }
       // Epilogue: D = C + acc, masked stores.
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -314,50 +427,27 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         for (int j = 0; j < FN; ++j) {
           const int gn = n0 + wn * TN + j * 16 + 4 * q4;
           if (gn >= p.n) continue;
-          f32x4 v = acc[i][j];
-          const bool full = gn + 4 <= p.n;
-          if (HAS_C) {
-            const int64_t crow = (int64_t)gm * p.ldc;
-            if (BF16_OUT) {
-              const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (full || gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
-            } else {
-              const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
-              if (full) {
-                v += *reinterpret_cast<const f32x4*>(C);
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (gn + r < p.n) v[r] += C[r];
-              }
-            }
-          }
-          if (BF16_OUT) {
-            uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
-            if (full) {
-              const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-              const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
-              *reinterpret_cast<uint2*>(D) = make_uint2(lo, hi);
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (gn + r < p.n) D[r] = (uint16_t)bf16_rne_bits(v[r]);
-            }
-          } else {
-            float* D = reinterpret_cast<float*>(p.d) + drow + gn;
-            if (full) {
-              *reinterpret_cast<f32x4*>(D) = v;
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (gn + r < p.n) D[r] = v[r];
-            }
-          }
+          store_out<BF16_OUT, HAS_C>(p, gm, gn, drow, acc[i][j]);
         }
       }
     }
+  }
+}
+
+// Split-K reduction: D = C + sum over splits (in split order) of the FP32
+// partials ws[s][m][n]; one thread per 4 consecutive columns of a row.
+template <bool BF16_OUT, bool HAS_C>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const Params p) {
+  const int vec_per_row = (p.n + 3) >> 2;
+  const int64_t total = (int64_t)p.m * vec_per_row;
+  const int64_t split_stride = (int64_t)p.m * p.ldw;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int gm = (int)(idx / vec_per_row);
+    const int gn = (int)(idx - (int64_t)gm * vec_per_row) * 4;
+    const float* W = p.ws + (int64_t)gm * p.ldw + gn;
+    f32x4 v = *reinterpret_cast<const f32x4*>(W);
+    for (int s = 1; s < p.splits; ++s) v += *reinterpret_cast<const f32x4*>(W + s * split_stride);
+    store_out<BF16_OUT, HAS_C>(p, gm, gn, (int64_t)gm * p.ldd, v);
   }
 }
 

@@ -207,3 +207,18 @@ def test_num_cus_cap_gives_same_bits():
         assert np.array_equal(raw_bits(run_dense(x)), ref_bits)
     finally:
         dg.set_num_cus(0)
+
+
+@pytest.mark.parametrize("m,out", [(48, "fp32"), (128, "bf16"), (100, "fp32")])
+def test_dense_split_k_with_c(m, out):
+    """Skinny M takes the split-K path (FP32 partials + ordered reduction); C is added once."""
+    x = gen_dense(m, 520, 2048, seed=60 + m, with_c=True, out_dtype=out)
+    _check_dense(x, run_dense(x, ld_d=528), f"split-K + C M={m} {out}")
+
+
+def test_split_k_determinism_and_sentinel_columns():
+    x = gen_dense(64, 2112, 7168, seed=61)
+    d1 = run_dense(x, ld_d=2120)
+    d2 = run_dense(x, ld_d=2120)
+    assert np.array_equal(raw_bits(d1), raw_bits(d2))
+    _check_dense(x, d1, "split-K M=64 N=2112 K=7168")
