@@ -295,8 +295,10 @@ def main():
               file=sys.stderr, flush=True)
 
     # per-launch timing, warm (back to back) and cold (after a cache flush)
-    flush_buf = torch.empty(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
-    flush = lambda: flush_buf.fill_(1.0)
+    # read-only flush: evicts the operands from L2 and the Infinity Cache without
+    # leaving dirty lines whose write-back would overlap the timed launch
+    flush_buf = torch.ones(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.sum()
     detail = []
     for c in cases:
         c.call()

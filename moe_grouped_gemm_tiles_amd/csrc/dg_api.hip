@@ -32,11 +32,14 @@ std::atomic<int> g_num_cus{-1};  // -1: not yet read from the environment
 int g_device_cus[kMaxDevices] = {0};
 std::once_flag g_env_once;
 bool g_print_configs = false;
+int g_force_splits = 0;
 
 void read_env() {
   std::call_once(g_env_once, [] {
     const char* s = std::getenv("DG_PRINT_CONFIGS");
     g_print_configs = s && std::atoi(s) != 0;
+    const char* f = std::getenv("DG_FORCE_SPLITS");
+    g_force_splits = f ? std::atoi(f) : 0;
     int expected = -1;
     const char* c = std::getenv("DG_NUM_CUS");
     const int v = c ? std::atoi(c) : 0;
@@ -89,10 +92,11 @@ KernelFn pick_reduce(dg_dtype t, bool has_c) {
 // Tile configurations.  LDS per workgroup = stages x ((BM + BN) x 128 B + BM x 4 B):
 //   256x256, 8 waves, 2 stages: 130 KiB (one workgroup per CU) -- large M and N
 //   128x128, 4 waves, 2 stages:  65 KiB (two per CU)           -- small grouped tiles
-//   128x128, 4 waves, 4 stages: 130 KiB, split-K              -- dense 64 < M <= 128
-//    64x128, 4 waves, 4 stages:  97 KiB, split-K              -- dense M <= 64
-// The split-K configurations stream B from HBM with three slabs in flight.
-enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x128 = 2, TILE_SK_64x128 = 3 };
+//   128x64,  4 waves, 3 stages:  74 KiB (two per CU), split-K  -- dense 64 < M <= 128
+//    64x128, 4 waves, 3 stages:  73 KiB (two per CU), split-K  -- dense M <= 64
+// The split-K configurations stream B from HBM; two independent workgroups
+// per CU keep four slabs in flight per CU.
+enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x64 = 2, TILE_SK_64x128 = 3 };
 
 struct Cfg {
   TileId id;
@@ -101,16 +105,16 @@ struct Cfg {
 
 constexpr Cfg kCfg256{TILE_256x256, 256, 256, 2, 4, 2, 1};
 constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
-constexpr Cfg kCfgSk128{TILE_SK_128x128, 128, 128, 2, 2, 4, 1};
-constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 4, 1};
+constexpr Cfg kCfgSk128{TILE_SK_128x64, 128, 64, 2, 2, 3, 2};
+constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 3, 2};
 
 template <int MODE>
 KernelFn pick_kernel(const Cfg& c, bool split, dg_dtype t, bool has_c) {
   if constexpr (MODE == dg::MODE_DENSE) {
-    if (c.id == TILE_SK_128x128)
-      return split ? dg::gemm_kernel<128, 128, 2, 2, 4, MODE, true, false, false> : pick_epilogue<128, 128, 2, 2, 4, MODE>(t, has_c);
+    if (c.id == TILE_SK_128x64)
+      return split ? dg::gemm_kernel<128, 64, 2, 2, 3, MODE, true, false, false> : pick_epilogue<128, 64, 2, 2, 3, MODE>(t, has_c);
     if (c.id == TILE_SK_64x128)
-      return split ? dg::gemm_kernel<64, 128, 1, 4, 4, MODE, true, false, false> : pick_epilogue<64, 128, 1, 4, 4, MODE>(t, has_c);
+      return split ? dg::gemm_kernel<64, 128, 1, 4, 3, MODE, true, false, false> : pick_epilogue<64, 128, 1, 4, 3, MODE>(t, has_c);
   }
   (void)split;
   if (c.id == TILE_256x256) return pick_epilogue<256, 256, 2, 4, 2, MODE>(t, has_c);
@@ -192,9 +196,14 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int grou
   if (st != DG_SUCCESS) return st;
   const int slots = cus * cfg.per_cu;
   bool split = false;
-  if (MODE == dg::MODE_DENSE && (cfg.id == TILE_SK_128x128 || cfg.id == TILE_SK_64x128) && p.k >= 128 * 8) {
+  if (MODE == dg::MODE_DENSE && (cfg.id == TILE_SK_128x64 || cfg.id == TILE_SK_64x128) && p.k >= 128 * 8) {
     int sps = 0;
-    const int s = choose_splits(p.tiles_m * p.tiles_n, p.k / 128, slots, &sps);
+    int s = choose_splits(p.tiles_m * p.tiles_n, p.k / 128, slots, &sps);
+    if (g_force_splits > 0) {  // tuning knob: DG_FORCE_SPLITS
+      const int kb = p.k / 128;
+      sps = cdiv(kb, g_force_splits < kb ? g_force_splits : kb);
+      s = cdiv(kb, sps);
+    }
     if (s > 1) {
       split = true;
       p.splits = s;
