@@ -135,7 +135,85 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
                                           int num_groups, int m_max, int n, int k,
                                           int expected_m, hipStream_t stream);
 
-/* Row alignment of expert segments in the contiguous layout (128).
+/*
+ * UE8M0 variants of the three GEMMs above.  [README] "Interfaces > Notices":
+ * the newer architecture takes UE8M0 scale factors, four packed into one
+ * 32-bit integer, instead of FP32.  Same granularity as the FP32 form (A per
+ * (row, 128-K block), B per 128x128 block); each byte e means 2^(e-127), 255
+ * is NaN.  Packing runs along K: byte j (least significant first) of word q
+ * holds the scale of K block 4q + j; bytes past the last K block are ignored.
+ * On gfx950 the scales feed the MFMA's block-scale operands, so the K loop
+ * accumulates in the matrix core without FP32 promotion.
+ *
+ * sfa   int32 words [ceil(k/512)][ld_sfa] (masked: [num_groups][ceil(k/512)][ld_sfa]),
+ *       ld_sfa >= rows of A, ld_sfa % 4 == 0, 16-B aligned.
+ * sfb   int32 words [ceil(n/128)][ceil(k/512)] (grouped: [num_groups][...]), 4-B aligned.
+ * All other arguments, layouts and errors as in the FP32-scale entry points.
+ */
+dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t ld_sfa,
+                               const void* b, int64_t ldb, const int32_t* sfb,
+                               const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
+                               int m, int n, int k, hipStream_t stream);
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
+                                                    const void* b, const int32_t* sfb,
+                                                    void* d, dg_dtype d_dtype,
+                                                    const int32_t* m_indices,
+                                                    int m_total, int n, int k, int num_groups,
+                                                    hipStream_t stream);
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
+                                                const void* b, const int32_t* sfb,
+                                                void* d, dg_dtype d_dtype,
+                                                const int32_t* masked_m,
+                                                int num_groups, int m_max, int n, int k,
+                                                int expected_m, hipStream_t stream);
+
+/*
+ * K-grouped GEMM (MoE weight gradient):
+ *   [README] "Grouped GEMMs (contiguous layout)": a K-axis-grouped API for the
+ *   MoE weight backward, with M and N fixed; the pull-request text on the
+ *   same page: FP8 x FP8 -> FP32 weight-gradient GEMMs for dense and MoE models.
+ *
+ * Group g owns K range [k_off[g], k_off[g] + ks[g]) where k_off is the
+ * exclusive prefix sum of ks, and D[g] = C[g] + A[:, range] @ B[:, range]^T.
+ *
+ * a        E4M3 [m, k_total] contiguous (row stride k_total): K-contiguous ("NT");
+ *          token-major tensors are transposed by the caller.
+ * sfa      FP32 [k_total/128][ld_sfa], ld_sfa >= m, ld_sfa % 4 == 0 (scales by
+ *          global K block).
+ * b        E4M3 [n, k_total] contiguous.
+ * sfb      FP32 [ceil(n/128)][k_total/128].
+ * c        optional FP32 [num_groups, m, n] contiguous (NULL = zero); may equal d.
+ * d        FP32 [num_groups, m, n] contiguous.  Every group's D is written, also
+ *          for ks[g] == 0 (then D[g] = C[g] or 0).
+ * ks       DEVICE int32 [num_groups]: K size of each group, a multiple of 128
+ *          (dg_get_mk_alignment_for_contiguous_layout).  Device data is clamped,
+ *          never an error: negative sizes count as 0, sizes round down to a
+ *          multiple of 128, and ranges past k_total are cut at k_total.
+ * k_total  sum of ks; k_total % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa,
+                                              const void* b, const float* sfb,
+                                              const float* c, float* d, const int32_t* ks,
+                                              int num_groups, int m, int n, int k_total,
+                                              hipStream_t stream);
+
+/*
+ * Weight-gradient GEMMs with FP32 accumulation in place (the pull request on
+ * the page "Weight gradient kernels for dense and MoE models #95"):
+ *   dg_wgrad_fp8_gemm_nt            D[m,n] += A[m,k] @ B[n,k]^T           (dense)
+ *   dg_k_grouped_wgrad_fp8_gemm_nt  D[g]   += A[:, K_g] @ B[:, K_g]^T      (K-grouped)
+ * They are dg_fp8_gemm_nt with c = d (FP32) and dg_k_grouped_fp8_gemm_nt_contiguous
+ * with c = d; arguments as there.
+ */
+dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
+                               const void* b, int64_t ldb, const float* sfb,
+                               float* d, int64_t ldd, int m, int n, int k, hipStream_t stream);
+dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_t ld_sfa,
+                                         const void* b, const float* sfb, float* d, const int32_t* ks,
+                                         int num_groups, int m, int n, int k_total, hipStream_t stream);
+
+/* Row (M-grouped) and K (K-grouped) alignment of group segments in the
+ * contiguous layouts (128).
  * [README] "Utilities": get_mk_alignment_for_contiguous_layout. */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

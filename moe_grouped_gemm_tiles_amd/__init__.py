@@ -10,8 +10,15 @@ as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
 * ``fp8_gemm_nt((a, sfa), (b, sfb), d, c=None)``
 * ``m_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, m_indices)``
 * ``m_grouped_fp8_gemm_nt_masked((a, sfa), (b, sfb), d, masked_m, expected_m)``
+* ``k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c=None)``
+* ``wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d)`` and
+  ``k_grouped_wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d, ks)`` (D += ..., FP32)
 * ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
   ``set_num_cus(n)`` / ``get_num_cus()``
+
+The three M-side GEMMs take either FP32 scales or UE8M0 scales packed four
+per int32 along K (the README's "Interfaces > Notices" names both formats);
+the binding picks the entry point from the scale tensors' dtype.
 
 Operands follow the ``(tensor, scale)`` pair convention of the README:
 ``a`` is E4M3 (``torch.float8_e4m3fn`` or ``torch.uint8`` codes) ``[M, K]``
@@ -19,6 +26,9 @@ Operands follow the ``(tensor, scale)`` pair convention of the README:
 (masked: ``[G, K/128, ld]``), ``b`` is E4M3 ``[N, K]`` (grouped
 ``[G, N, K]``), ``sfb`` is FP32 ``[ceil(N/128), K/128]`` (grouped
 ``[G, ceil(N/128), K/128]``), ``d`` is a caller-allocated BF16 or FP32 tensor.
+With UE8M0 scales, ``sfa`` is int32 ``[ceil(K/512), ld]`` (masked
+``[G, ceil(K/512), ld]``) and ``sfb`` int32 ``[ceil(N/128), ceil(K/512)]``
+(grouped ``[G, ...]``).
 """
 
 from __future__ import annotations
@@ -32,6 +42,9 @@ __all__ = [
     "fp8_gemm_nt",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
+    "k_grouped_fp8_gemm_nt_contiguous",
+    "wgrad_fp8_gemm_nt",
+    "k_grouped_wgrad_fp8_gemm_nt",
     "get_mk_alignment_for_contiguous_layout",
     "get_sf_aligned_size",
     "set_num_cus",
@@ -58,6 +71,16 @@ _SIGNATURES = {
                                                    _i32, _i32, _i32, _i32, _vp]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _vp]),
+    "dg_fp8_gemm_nt_ue8m0": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
+                                    _i32, _i32, _i32, _vp]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                                                         _i32, _i32, _i32, _i32, _vp]),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                                                     _i32, _i32, _i32, _i32, _i32, _vp]),
+    "dg_k_grouped_fp8_gemm_nt_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                                                   _i32, _i32, _i32, _i32, _vp]),
+    "dg_wgrad_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "dg_k_grouped_wgrad_fp8_gemm_nt": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
@@ -104,6 +127,21 @@ def _unit_last_stride(t: torch.Tensor) -> bool:
     return t.numel() == 0 or t.size(-1) == 1 or t.stride(-1) == 1
 
 
+def _ld(t: torch.Tensor, dim: int = 0, align: int = 1) -> int:
+    """Leading dimension (elements between consecutive indices of ``dim``).
+
+    A dimension of size 1 may carry any stride in torch (and numpy), so there
+    the dense row length, rounded up to ``align`` elements, is passed instead;
+    the library never steps along that dimension then.
+    """
+    if t.size(dim) > 1:
+        return t.stride(dim)
+    row = 1
+    for s in t.shape[dim + 1:]:
+        row *= s
+    return (row + align - 1) // align * align
+
+
 def _fp8(t: torch.Tensor, name: str):
     if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
         raise TypeError(f"{name} must be torch.float8_e4m3fn or uint8 codes, got {t.dtype}")
@@ -120,6 +158,23 @@ def _f32(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous in its last dimension")
 
 
+def _sf(sfa: torch.Tensor, sfb: torch.Tensor) -> bool:
+    """Checks a scale pair; True for packed UE8M0 (int32), False for FP32."""
+    if sfa.dtype != sfb.dtype or sfa.dtype not in (torch.float32, torch.int32):
+        raise TypeError("sfa and sfb must both be float32 (FP32 scales) or both int32 (packed UE8M0)")
+    for t, nm in ((sfa, "sfa"), (sfb, "sfb")):
+        if not t.is_cuda:
+            raise TypeError(f"{nm} must be a GPU tensor")
+        if not _unit_last_stride(t):
+            raise ValueError(f"{nm} must be contiguous in its last dimension")
+    return sfa.dtype == torch.int32
+
+
+def _sf_rows(k: int, ue8m0: bool) -> int:
+    """Scale rows along K: K/128 FP32 scales, or ceil(K/512) packed UE8M0 words."""
+    return (k // 128 + 3) // 4 if ue8m0 else k // 128
+
+
 def _out(t: torch.Tensor, name: str = "d") -> int:
     if t.dtype not in _DTYPES or not t.is_cuda:
         raise TypeError(f"{name} must be a bfloat16 or float32 GPU tensor")
@@ -134,30 +189,31 @@ def _dense_contig(t: torch.Tensor, name: str):
 
 
 def fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, c: torch.Tensor | None = None):
-    """D = C + A @ B.T with A [M,K], B [N,K] E4M3 and FP32 fine-grained scales."""
+    """D = C + A @ B.T with A [M,K], B [N,K] E4M3 and FP32 or packed-UE8M0 fine-grained scales."""
     lib = load_library()
     a, sfa = a_pair
     b, sfb = b_pair
     _fp8(a, "a")
     _fp8(b, "b")
-    _f32(sfa, "sfa")
-    _f32(sfb, "sfb")
+    ue = _sf(sfa, sfb)
     _dense_contig(sfb, "sfb")
     dt = _out(d)
     m, k = a.shape
     n = b.shape[0]
     if b.shape[1] != k or d.shape != (m, n):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, d {tuple(d.shape)}")
-    if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
+    kr = _sf_rows(k, ue)
+    if sfa.dim() != 2 or sfa.shape[0] != kr or sfb.shape != ((n + 127) // 128, kr):
         raise ValueError(f"scale shapes: sfa {tuple(sfa.shape)}, sfb {tuple(sfb.shape)}")
     c_ptr, ldc = None, 0
     if c is not None:
         if c.dtype != d.dtype or c.shape != d.shape or not _unit_last_stride(c) or not c.is_cuda:
             raise ValueError("c must match d's dtype and shape")
-        c_ptr, ldc = c.data_ptr(), c.stride(0)
-    st = lib.dg_fp8_gemm_nt(a.data_ptr(), a.stride(0), sfa.data_ptr(), sfa.stride(0),
-                            b.data_ptr(), b.stride(0), sfb.data_ptr(),
-                            c_ptr, ldc, d.data_ptr(), d.stride(0), dt, m, n, k, _stream(d))
+        c_ptr, ldc = c.data_ptr(), _ld(c, 0, 16 // c.element_size())
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if ue else lib.dg_fp8_gemm_nt
+    es = d.element_size()
+    st = fn(a.data_ptr(), _ld(a, 0, 16), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(), _ld(b, 0, 16),
+            sfb.data_ptr(), c_ptr, ldc, d.data_ptr(), _ld(d, 0, 16 // es), dt, m, n, k, _stream(d))
     _check(st)
     return d
 
@@ -171,8 +227,7 @@ def m_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, m_indices:
         _dense_contig(t, nm)
     _fp8(a, "a")
     _fp8(b, "b")
-    _f32(sfa, "sfa")
-    _f32(sfb, "sfb")
+    ue = _sf(sfa, sfb)
     dt = _out(d)
     if m_indices.dtype != torch.int32 or not m_indices.is_cuda:
         raise TypeError("m_indices must be an int32 GPU tensor")
@@ -180,11 +235,12 @@ def m_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, m_indices:
     g, n, kb_ = b.shape
     if kb_ != k or d.shape != (m_total, n) or m_indices.shape != (m_total,):
         raise ValueError("shape mismatch")
-    if sfa.shape[0] != k // 128 or sfb.shape != (g, (n + 127) // 128, k // 128):
+    kr = _sf_rows(k, ue)
+    if sfa.dim() != 2 or sfa.shape[0] != kr or sfb.shape != (g, (n + 127) // 128, kr):
         raise ValueError("scale shape mismatch")
-    st = lib.dg_m_grouped_fp8_gemm_nt_contiguous(a.data_ptr(), sfa.data_ptr(), sfa.stride(0),
-                                                 b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
-                                                 m_indices.data_ptr(), m_total, n, k, g, _stream(d))
+    fn = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if ue else lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    st = fn(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
+            m_indices.data_ptr(), m_total, n, k, g, _stream(d))
     _check(st)
     return d
 
@@ -199,8 +255,7 @@ def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d: torch.Tensor, masked_m: torc
         _dense_contig(t, nm)
     _fp8(a, "a")
     _fp8(b, "b")
-    _f32(sfa, "sfa")
-    _f32(sfb, "sfb")
+    ue = _sf(sfa, sfb)
     dt = _out(d)
     if masked_m.dtype != torch.int32 or not masked_m.is_cuda:
         raise TypeError("masked_m must be an int32 GPU tensor")
@@ -208,12 +263,86 @@ def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d: torch.Tensor, masked_m: torc
     n = b.shape[1]
     if b.shape != (g, n, k) or d.shape != (g, m_max, n) or masked_m.shape != (g,):
         raise ValueError("shape mismatch")
-    if sfa.dim() != 3 or sfa.shape[:2] != (g, k // 128) or sfb.shape != (g, (n + 127) // 128, k // 128):
+    kr = _sf_rows(k, ue)
+    if sfa.dim() != 3 or sfa.shape[:2] != (g, kr) or sfb.shape != (g, (n + 127) // 128, kr):
         raise ValueError("scale shape mismatch")
-    st = lib.dg_m_grouped_fp8_gemm_nt_masked(a.data_ptr(), sfa.data_ptr(), sfa.stride(1),
-                                             b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
-                                             masked_m.data_ptr(), g, m_max, n, k, int(expected_m),
-                                             _stream(d))
+    fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if ue else lib.dg_m_grouped_fp8_gemm_nt_masked
+    st = fn(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 1, 4), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
+            masked_m.data_ptr(), g, m_max, n, k, int(expected_m), _stream(d))
+    _check(st)
+    return d
+
+
+def _k_grouped_args(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor):
+    a, sfa = a_pair
+    b, sfb = b_pair
+    for t, nm in ((a, "a"), (b, "b"), (sfb, "sfb"), (d, "d"), (ks, "ks")):
+        _dense_contig(t, nm)
+    _fp8(a, "a")
+    _fp8(b, "b")
+    _f32(sfa, "sfa")
+    _f32(sfb, "sfb")
+    if d.dtype != torch.float32 or not d.is_cuda:
+        raise TypeError("d must be a float32 GPU tensor")
+    if ks.dtype != torch.int32 or not ks.is_cuda:
+        raise TypeError("ks must be an int32 GPU tensor")
+    m, k = a.shape
+    n = b.shape[0]
+    g = ks.shape[0]
+    if b.shape != (n, k) or d.shape != (g, m, n) or ks.dim() != 1:
+        raise ValueError("shape mismatch")
+    if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    return a, sfa, b, sfb, g, m, n, k
+
+
+def k_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor,
+                                     c: torch.Tensor | None = None):
+    """K-grouped GEMM: D[g] = C[g] + A[:, K_g] @ B[:, K_g].T (FP32), K_g given by ks (int32, device)."""
+    lib = load_library()
+    a, sfa, b, sfb, g, m, n, k = _k_grouped_args(a_pair, b_pair, d, ks)
+    c_ptr = None
+    if c is not None:
+        if c.dtype != torch.float32 or c.shape != d.shape or not c.is_contiguous() or not c.is_cuda:
+            raise ValueError("c must be a contiguous float32 GPU tensor shaped like d")
+        c_ptr = c.data_ptr()
+    st = lib.dg_k_grouped_fp8_gemm_nt_contiguous(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
+                                                 sfb.data_ptr(), c_ptr, d.data_ptr(), ks.data_ptr(), g, m, n, k,
+                                                 _stream(d))
+    _check(st)
+    return d
+
+
+def wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor):
+    """Dense weight gradient: D += A @ B.T in FP32 (D is read and written)."""
+    lib = load_library()
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _fp8(a, "a")
+    _fp8(b, "b")
+    _f32(sfa, "sfa")
+    _f32(sfb, "sfb")
+    _dense_contig(sfb, "sfb")
+    if d.dtype != torch.float32 or not d.is_cuda or not _unit_last_stride(d):
+        raise TypeError("d must be a float32 GPU tensor, contiguous in its last dimension")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or d.shape != (m, n):
+        raise ValueError("shape mismatch")
+    if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    st = lib.dg_wgrad_fp8_gemm_nt(a.data_ptr(), _ld(a, 0, 16), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
+                                  _ld(b, 0, 16), sfb.data_ptr(), d.data_ptr(), _ld(d, 0, 4), m, n, k, _stream(d))
+    _check(st)
+    return d
+
+
+def k_grouped_wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor):
+    """K-grouped weight gradient: D[g] += A[:, K_g] @ B[:, K_g].T in FP32."""
+    lib = load_library()
+    a, sfa, b, sfb, g, m, n, k = _k_grouped_args(a_pair, b_pair, d, ks)
+    st = lib.dg_k_grouped_wgrad_fp8_gemm_nt(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
+                                            sfb.data_ptr(), d.data_ptr(), ks.data_ptr(), g, m, n, k, _stream(d))
     _check(st)
     return d
 

@@ -75,20 +75,6 @@ inline int64_t dtype_size(dg_dtype t) { return t == DG_DTYPE_BF16 ? 2 : 4; }
 
 using KernelFn = void (*)(dg::Params);
 
-template <int BM, int BN, int WM, int WN, int ST, int MODE>
-KernelFn pick_epilogue(dg_dtype t, bool has_c) {
-  if (t == DG_DTYPE_BF16)
-    return has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, true>
-                 : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false>;
-  return has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true>
-               : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false>;
-}
-
-KernelFn pick_reduce(dg_dtype t, bool has_c) {
-  if (t == DG_DTYPE_BF16) return has_c ? dg::splitk_reduce_kernel<true, true> : dg::splitk_reduce_kernel<true, false>;
-  return has_c ? dg::splitk_reduce_kernel<false, true> : dg::splitk_reduce_kernel<false, false>;
-}
-
 // Tile configurations.  LDS per workgroup = stages x ((BM + BN) x 128 B + BM x 4 B):
 //   256x256, 8 waves, 2 stages: 130 KiB (one workgroup per CU) -- large M and N
 //   128x128, 4 waves, 2 stages:  65 KiB (two per CU)           -- small grouped tiles
@@ -108,21 +94,61 @@ constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
 constexpr Cfg kCfgSk128{TILE_SK_128x64, 128, 64, 2, 2, 3, 2};
 constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 3, 2};
 
-template <int MODE>
-KernelFn pick_kernel(const Cfg& c, bool split, dg_dtype t, bool has_c) {
+// Output flavour of a launch: split-K partials, or the final D with or without C.
+struct Epi {
+  bool split, bf16, has_c, e8m0;
+};
+
+// Only the combinations the entry points can reach are instantiated:
+// dense: every tile, BF16/FP32, with/without C, split partials for the skinny
+// tiles; M-grouped: 256x256 and 128x128 without C; K-grouped: FP32 with/without C.
+template <int BM, int BN, int WM, int WN, int ST, int MODE, bool E8M0>
+KernelFn pick_out(const Epi& e) {
+  constexpr bool kSkinny = BM < 128 || BN < 128;
   if constexpr (MODE == dg::MODE_DENSE) {
-    if (c.id == TILE_SK_128x64)
-      return split ? dg::gemm_kernel<128, 64, 2, 2, 3, MODE, true, false, false> : pick_epilogue<128, 64, 2, 2, 3, MODE>(t, has_c);
-    if (c.id == TILE_SK_64x128)
-      return split ? dg::gemm_kernel<64, 128, 1, 4, 3, MODE, true, false, false> : pick_epilogue<64, 128, 1, 4, 3, MODE>(t, has_c);
+    if constexpr (kSkinny)
+      if (e.split) return dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, true, false, false, E8M0>;
+    if (e.bf16)
+      return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, true, E8M0>
+                     : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false, E8M0>;
+    return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true, E8M0>
+                   : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
+  } else if constexpr (MODE == dg::MODE_KGROUP) {
+    return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true, E8M0>
+                   : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
+  } else {
+    return e.bf16 ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false, E8M0>
+                  : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
   }
-  (void)split;
-  if (c.id == TILE_256x256) return pick_epilogue<256, 256, 2, 4, 2, MODE>(t, has_c);
-  return pick_epilogue<128, 128, 2, 2, 2, MODE>(t, has_c);
+}
+
+KernelFn pick_reduce(dg_dtype t, bool has_c) {
+  if (t == DG_DTYPE_BF16) return has_c ? dg::splitk_reduce_kernel<true, true> : dg::splitk_reduce_kernel<true, false>;
+  return has_c ? dg::splitk_reduce_kernel<false, true> : dg::splitk_reduce_kernel<false, false>;
+}
+
+template <int MODE, bool E8M0>
+KernelFn pick_tile(const Cfg& c, const Epi& e) {
+  if constexpr (MODE == dg::MODE_DENSE) {
+    if (c.id == TILE_SK_128x64) return pick_out<128, 64, 2, 2, 3, MODE, E8M0>(e);
+    if (c.id == TILE_SK_64x128) return pick_out<64, 128, 1, 4, 3, MODE, E8M0>(e);
+  }
+  if (c.id == TILE_256x256) return pick_out<256, 256, 2, 4, 2, MODE, E8M0>(e);
+  return pick_out<128, 128, 2, 2, 2, MODE, E8M0>(e);
+}
+
+template <int MODE>
+KernelFn pick_kernel(const Cfg& c, const Epi& e) {
+  if constexpr (MODE == dg::MODE_KGROUP) {
+    return pick_tile<MODE, false>(c, e);
+  } else {
+    return e.e8m0 ? pick_tile<MODE, true>(c, e) : pick_tile<MODE, false>(c, e);
+  }
 }
 
 const char* mode_name(int mode) {
-  return mode == dg::MODE_DENSE ? "dense" : mode == dg::MODE_CONTIG ? "contiguous" : "masked";
+  return mode == dg::MODE_DENSE ? "dense" : mode == dg::MODE_CONTIG ? "contiguous"
+       : mode == dg::MODE_MASKED ? "masked" : "k-grouped";
 }
 
 // ---- split-K workspace: one growable FP32 buffer per (device, stream) --------
@@ -183,7 +209,7 @@ int choose_splits(int tiles, int kb, int slots, int* slabs_per_split) {
 }
 
 template <int MODE>
-dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int groups_for_tiles,
+dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, bool e8m0, int groups_for_tiles,
                  hipStream_t stream) {
   p.tiles_m = cdiv(p.m, cfg.bm);
   p.tiles_n = cdiv(p.n, cfg.bn);
@@ -216,13 +242,13 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int grou
   p.num_tiles = p.tiles_m * p.tiles_n * groups_for_tiles * p.splits;
   if (p.num_tiles <= 0) return DG_SUCCESS;
   const int grid = p.num_tiles < slots ? p.num_tiles : slots;
-  KernelFn fn = pick_kernel<MODE>(cfg, split, t, has_c);
+  KernelFn fn = pick_kernel<MODE>(cfg, Epi{split, t == DG_DTYPE_BF16, has_c, e8m0});
   if (g_print_configs)
     std::fprintf(stderr,
-                 "dg: %s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d stages=%d splits=%d (x%d slabs) "
+                 "dg: %s%s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d stages=%d splits=%d (x%d slabs) "
                  "tiles=%d grid=%d cus=%d\n",
-                 mode_name(MODE), p.m, p.n, p.k, p.num_groups, cfg.bm, cfg.bn, cfg.wm, cfg.wn, cfg.stages, p.splits,
-                 p.slabs_per_split, p.num_tiles, grid, cus);
+                 mode_name(MODE), e8m0 ? " ue8m0" : "", p.m, p.n, p.k, p.num_groups, cfg.bm, cfg.bn, cfg.wm, cfg.wn,
+                 cfg.stages, p.splits, p.slabs_per_split, p.num_tiles, grid, cus);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(cfg.wm * cfg.wn * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
@@ -237,8 +263,9 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, int grou
   return DG_SUCCESS;
 }
 
-// Shared operand checks; rows = rows of A (M, M_total or M_max).
-dg_status check_common(const void* a, const float* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+// Shared operand checks; rows = rows of A (M, M_total or M_max).  Both scale
+// forms use 4-byte elements (FP32 values or packed UE8M0 words).
+dg_status check_common(const void* a, const void* sfa, int64_t ld_sfa, const void* b, const void* sfb,
                        const void* d, dg_dtype t, int rows, int n, int k) {
   if (rows < 0 || n < 0 || k < 0) return DG_ERROR_INVALID_VALUE;
   if (t != DG_DTYPE_BF16 && t != DG_DTYPE_FP32) return DG_ERROR_INVALID_VALUE;
@@ -253,13 +280,14 @@ dg_status check_common(const void* a, const float* sfa, int64_t ld_sfa, const vo
   return DG_SUCCESS;
 }
 
-}  // namespace
+// Rows of sfb per 128-column block: K blocks (FP32) or packed words (UE8M0).
+inline int64_t sfb_row(int k, bool e8m0) { return e8m0 ? (k / 128 + 3) / 4 : k / 128; }
+// Rows of sfa per group: K blocks (FP32) or packed words (UE8M0).
+inline int64_t sfa_rows(int k, bool e8m0) { return sfb_row(k, e8m0); }
 
-extern "C" {
-
-dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
-                         int64_t ldb, const float* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
-                         dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
+dg_status dense_impl(const void* a, int64_t lda, const void* sfa, int64_t ld_sfa, const void* b, int64_t ldb,
+                     const void* sfb, const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype, int m,
+                     int n, int k, bool e8m0, hipStream_t stream) {
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m, n, k);
   if (st != DG_SUCCESS) return st;
   const int64_t es = dtype_size(d_dtype);
@@ -270,9 +298,9 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
 
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
-  p.sfa = sfa;
+  p.sfa = static_cast<const float*>(sfa);
   p.b = static_cast<const uint8_t*>(b);
-  p.sfb = sfb;
+  p.sfb = static_cast<const float*>(sfb);
   p.c = c;
   p.d = d;
   p.grp = nullptr;
@@ -288,13 +316,12 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
   if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
     return DG_ERROR_NOT_SUPPORTED;
   const Cfg cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? kCfg256 : kCfg128);
-  return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, 1, stream);
+  return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, e8m0, 1, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
-                                              const float* sfb, void* d, dg_dtype d_dtype,
-                                              const int32_t* m_indices, int m_total, int n, int k,
-                                              int num_groups, hipStream_t stream) {
+dg_status contiguous_impl(const void* a, const void* sfa, int64_t ld_sfa, const void* b, const void* sfb, void* d,
+                          dg_dtype d_dtype, const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                          bool e8m0, hipStream_t stream) {
   if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_total, n, k);
   if (st != DG_SUCCESS) return st;
@@ -305,9 +332,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, i
 
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
-  p.sfa = sfa;
+  p.sfa = static_cast<const float*>(sfa);
   p.b = static_cast<const uint8_t*>(b);
-  p.sfb = sfb;
+  p.sfb = static_cast<const float*>(sfb);
   p.c = nullptr;
   p.d = d;
   p.grp = m_indices;
@@ -316,20 +343,19 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, i
   p.ldd = n;
   p.ld_sfa = ld_sfa;
   p.b_gs = static_cast<int64_t>(n) * k;
-  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * (k / 128);
+  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * sfb_row(k, e8m0);
   p.m = m_total;
   p.n = n;
   p.k = k;
   p.num_groups = num_groups;
   if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
   const Cfg cfg = n > 128 ? kCfg256 : kCfg128;
-  return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, 1, stream);
+  return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, e8m0, 1, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
-                                          const float* sfb, void* d, dg_dtype d_dtype, const int32_t* masked_m,
-                                          int num_groups, int m_max, int n, int k, int expected_m,
-                                          hipStream_t stream) {
+dg_status masked_impl(const void* a, const void* sfa, int64_t ld_sfa, const void* b, const void* sfb, void* d,
+                      dg_dtype d_dtype, const int32_t* masked_m, int num_groups, int m_max, int n, int k,
+                      int expected_m, bool e8m0, hipStream_t stream) {
   if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_max, n, k);
   if (st != DG_SUCCESS) return st;
@@ -339,9 +365,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
 
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
-  p.sfa = sfa;
+  p.sfa = static_cast<const float*>(sfa);
   p.b = static_cast<const uint8_t*>(b);
-  p.sfb = sfb;
+  p.sfb = static_cast<const float*>(sfb);
   p.c = nullptr;
   p.d = d;
   p.grp = masked_m;
@@ -350,9 +376,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
   p.ldd = n;
   p.ld_sfa = ld_sfa;
   p.a_gs = static_cast<int64_t>(m_max) * k;
-  p.sfa_gs = static_cast<int64_t>(k / 128) * ld_sfa;
+  p.sfa_gs = sfa_rows(k, e8m0) * ld_sfa;
   p.b_gs = static_cast<int64_t>(n) * k;
-  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * (k / 128);
+  p.sfb_gs = static_cast<int64_t>(cdiv(n, 128)) * sfb_row(k, e8m0);
   p.d_gs = static_cast<int64_t>(m_max) * n;
   p.m = m_max;
   p.n = n;
@@ -361,7 +387,106 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
   if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
   const int em = expected_m > 0 ? expected_m : m_max;
   const Cfg cfg = (em > 128 && n > 128) ? kCfg256 : kCfg128;
-  return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, num_groups, stream);
+  return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, e8m0, num_groups, stream);
+}
+
+dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+                         const float* c, float* d, const int32_t* ks, int num_groups, int m, int n, int k_total,
+                         hipStream_t stream) {
+  if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
+  dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, DG_DTYPE_FP32, m, n, k_total);
+  if (st != DG_SUCCESS) return st;
+  if ((static_cast<int64_t>(n) * 4) % 16 != 0) return DG_ERROR_INVALID_VALUE;
+  if (c != nullptr && !aligned(c, 16)) return DG_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0 || num_groups == 0) return DG_SUCCESS;
+  if (ks == nullptr || !aligned(ks, 4)) return DG_ERROR_INVALID_VALUE;
+
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = c;
+  p.d = d;
+  p.grp = ks;
+  p.lda = k_total;
+  p.ldb = k_total;
+  p.ldc = n;
+  p.ldd = n;
+  p.ld_sfa = ld_sfa;
+  p.c_gs = static_cast<int64_t>(m) * n;
+  p.d_gs = static_cast<int64_t>(m) * n;
+  p.m = m;
+  p.n = n;
+  p.k = k_total;
+  p.num_groups = num_groups;
+  if (static_cast<int64_t>(k_total) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
+  const Cfg cfg = (m > 128 && n > 128) ? kCfg256 : kCfg128;
+  return launch<dg::MODE_KGROUP>(p, cfg, DG_DTYPE_FP32, c != nullptr, false, num_groups, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
+                         int64_t ldb, const float* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
+                         dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                              const float* sfb, void* d, dg_dtype d_dtype,
+                                              const int32_t* m_indices, int m_total, int n, int k,
+                                              int num_groups, hipStream_t stream) {
+  return contiguous_impl(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_indices, m_total, n, k, num_groups, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                          const float* sfb, void* d, dg_dtype d_dtype, const int32_t* masked_m,
+                                          int num_groups, int m_max, int n, int k, int expected_m,
+                                          hipStream_t stream) {
+  return masked_impl(a, sfa, ld_sfa, b, sfb, d, d_dtype, masked_m, num_groups, m_max, n, k, expected_m, false,
+                     stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t ld_sfa, const void* b,
+                               int64_t ldb, const int32_t* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
+                               dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
+                                                    const void* b, const int32_t* sfb, void* d, dg_dtype d_dtype,
+                                                    const int32_t* m_indices, int m_total, int n, int k,
+                                                    int num_groups, hipStream_t stream) {
+  return contiguous_impl(a, sfa, ld_sfa, b, sfb, d, d_dtype, m_indices, m_total, n, k, num_groups, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa, const void* b,
+                                                const int32_t* sfb, void* d, dg_dtype d_dtype,
+                                                const int32_t* masked_m, int num_groups, int m_max, int n, int k,
+                                                int expected_m, hipStream_t stream) {
+  return masked_impl(a, sfa, ld_sfa, b, sfb, d, d_dtype, masked_m, num_groups, m_max, n, k, expected_m, true,
+                     stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                              const float* sfb, const float* c, float* d, const int32_t* ks,
+                                              int num_groups, int m, int n, int k_total, hipStream_t stream) {
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, c, d, ks, num_groups, m, n, k_total, stream);
+}
+
+dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
+                               int64_t ldb, const float* sfb, float* d, int64_t ldd, int m, int n, int k,
+                               hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, d, ldd, d, ldd, DG_DTYPE_FP32, m, n, k, false, stream);
+}
+
+dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
+                                         const float* sfb, float* d, const int32_t* ks, int num_groups, int m,
+                                         int n, int k_total, hipStream_t stream) {
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, d, d, ks, num_groups, m, n, k_total, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return kAlignM; }

@@ -11,37 +11,42 @@
 //   promoted into higher-precision FP32 accumulators with FMAs that should
 //   overlap the matrix instructions.
 //
-// Design (gfx950; measured: FP8 MFMA ~4.0 PFLOP/s sustained, ~7 independent
-// FP32 FMAs co-issue per 16x16x128 MFMA, LDS reads ~128 B/clk/CU):
+// Design (gfx950; measured: FP8 MFMA ~4.0-4.6 PFLOP/s sustained depending on
+// clock, LDS b128 reads ~200 B/clk/CU, direct global->LDS loads ~60 B/clk/CU):
 //   * A workgroup owns a BM x BN output tile and walks K in 128-wide slabs;
 //     each slab is exactly one scale block along K.
 //   * Staging: buffer_load_dwordx4 ... lds copies each slab of A and B (and
 //     the slab's BM row scales of A) straight from global memory into LDS,
-//     double buffered, so the next slab streams in while the current one is
-//     multiplied.  The buffer descriptors end at the last valid row, so rows
-//     past M or N read as zero without any bounds arithmetic.  LDS rows are
-//     128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7), which the
-//     loads realise by permuting the global addresses (a direct load writes
-//     lane i's 16 bytes at LDS offset 16*i).  The 16 lanes of one fragment row
-//     group read K chunks q and q+4 (q = lane / 16), which together with the
-//     swizzle is free of bank conflicts (measured with SQ_LDS_BANK_CONFLICT;
-//     the more obvious chunks 2q, 2q+1 conflict 2-way on gfx950).
+//     through a ring of STAGES slab buffers, so later slabs stream in while
+//     the current one is multiplied.  The buffer descriptors end at the last
+//     valid row, so rows past M or N read as zero without any bounds
+//     arithmetic.  LDS rows are 128 bytes; 16-byte chunk c of row r sits at
+//     chunk c ^ (r & 7), which the loads realise by permuting the global
+//     addresses (a direct load writes lane i's 16 bytes at LDS offset 16*i).
+//     The 16 lanes of one fragment row group read K chunks q and q+4
+//     (q = lane / 16), which together with the swizzle is free of bank
+//     conflicts (measured with SQ_LDS_BANK_CONFLICT; the more obvious chunks
+//     2q, 2q+1 conflict 2-way on gfx950).
 //   * Each wave owns a TM x TN sub-tile of 16x16 MFMA tiles.  One
-//     v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K slab of a 16x16 tile,
-//     so a slab partial is a single instruction with a zero accumulator.  B is
-//     the MFMA's first operand and A the second: a lane's four results are
-//     four consecutive columns of one output row, so the row scale is one
+//     v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K slab of a 16x16 tile.
+//     B is the MFMA's first operand and A the second: a lane's four results
+//     are four consecutive columns of one output row, so the row scale is one
 //     value per lane per 16-row fragment and stores are 8/16-byte vectors.
-//   * Promotion: acc += P * (sfa[row] * sfb[block]) in FP32 after every slab.
-//     The FMAs of fragment i-1 are issued while the MFMAs of fragment i run
-//     (P is double buffered), which is how the FP32 promotion overlaps the
-//     matrix core here.
+//   * FP32 scales: each slab's partial comes out of the MFMA with a zero
+//     accumulator and is promoted, acc += P * (sfa[row] * sfb[block]), with
+//     FP32 FMAs.  The FMAs of MFMA t are issued after MFMA t+2 (a 3-deep ring
+//     of partials), so the promotion runs under the matrix core.
+//   * UE8M0 scales (powers of two): the MFMA's own block-scale operands apply
+//     sfa (per lane = per A row) and sfb (uniform per wave) to every 32-K
+//     chunk of the slab, and the MFMA accumulates straight into acc: no
+//     promotion at all.
 //   * Persistent grid, XCD-aware: workgroup b runs on XCD b % 8, so tile ids
 //     are renumbered so that the workgroups of one XCD take consecutive ids,
 //     and consecutive ids form compact (GM x n) blocks of tiles that share A
 //     and B panels in that XCD's L2.
 //   * Grouped variants resolve groups on device (contiguous: group index of a
-//     tile's 128-row halves; masked: masked_m), so the host never synchronises.
+//     tile's 128-row halves; masked: masked_m; K-grouped: prefix sums of the
+//     group K sizes), so the host never synchronises.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,7 +59,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+enum Mode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2, MODE_KGROUP = 3 };
 
 // Kernel arguments.  Strides in elements of the pointed-to type.
 struct Params {
@@ -64,9 +69,9 @@ struct Params {
   const float* sfb;
   const void* c;
   void* d;
-  const int32_t* grp;  // contiguous: m_indices[M]; masked: masked_m[G]
+  const int32_t* grp;  // contiguous: m_indices[M]; masked: masked_m[G]; K-grouped: ks[G]
   int64_t lda, ldb, ldc, ldd, ld_sfa;
-  int64_t a_gs, sfa_gs, b_gs, sfb_gs, d_gs;  // per-group strides
+  int64_t a_gs, sfa_gs, b_gs, sfb_gs, c_gs, d_gs;  // per-group strides
   int m, n, k, num_groups;
   int tiles_m, tiles_n, num_tiles;
   // split-K (dense only): K slabs are divided into `splits` ranges of
@@ -109,6 +114,19 @@ __device__ __forceinline__ float load_uniform_f32(const float* ptr) {
   return *reinterpret_cast<const float*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Workgroup barrier of the staging ring.  The caller has already waited for
+// its own loads of the slab about to be read (vmcnt); this adds the wait for
+// the wave's own LDS reads (a stage is overwritten only after every wave has
+// read it) and the barrier, but not the vmcnt(0) of __syncthreads(), which
+// would drain the loads of later slabs still in flight.  The empty asm
+// statements keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Raw buffer descriptor: loads at byte offsets >= num_bytes return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
@@ -129,6 +147,14 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void* ld
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 x, i32x8 y) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Block-scaled form accumulating into c: the low byte of sx (E8M0, 2^(e-127),
+// 255 = NaN) scales the 32 K-values lane l holds of x's row l%16, and sy
+// likewise for y (checked on gfx950: byte 127 is 1.0, the scale of a lane
+// applies to that lane's row and 32-K chunk only).
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128_e8m0(i32x8 x, i32x8 y, f32x4 c, int sx, int sy) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
 }
 
 // FP32 -> BF16, round to nearest even; NaN stays a quiet NaN.
@@ -166,13 +192,12 @@ __device__ __forceinline__ void raster(int t, int tm, int tn, int& mb, int& nb) 
   nb = r / gsz;
 }
 
-// D[gm][gn .. gn+3] = C + v (FP32 add, one rounding), columns past N dropped.
-// drow = element offset of row gm in D.
+// D[row][gn .. gn+3] = C + v (FP32 add, one rounding), columns past N dropped.
+// crow / drow = element offsets of the row in C / D.
 template <bool BF16_OUT, bool HAS_C>
-__device__ __forceinline__ void store_out(const Params& p, int gm, int gn, int64_t drow, f32x4 v) {
+__device__ __forceinline__ void store_out(const Params& p, int64_t crow, int gn, int64_t drow, f32x4 v) {
   const bool full = gn + 4 <= p.n;
   if (HAS_C) {
-    const int64_t crow = (int64_t)gm * p.ldc;
     if (BF16_OUT) {
       const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
 #pragma unroll
@@ -212,7 +237,10 @@ __device__ __forceinline__ void store_out(const Params& p, int gm, int gn, int64
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int MODE, bool SPLIT, bool BF16_OUT, bool HAS_C>
+// E8M0: sfa/sfb hold UE8M0 bytes packed four per 32-bit word along K
+// (byte j of word q = K block 4q + j): sfa words [KB/4 rounded up][ld_sfa],
+// sfb words [NB][KB/4 rounded up].  Otherwise FP32 sfa [KB][ld_sfa], sfb [NB][KB].
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE, bool SPLIT, bool BF16_OUT, bool HAS_C, bool E8M0>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -229,6 +257,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   static_assert(SFA_LANES >= 1 && SFA_LANES <= 64 && SFA_LANES * 16 == SFA_BYTES, "sfa staging");
   static_assert(MODE != MODE_CONTIG || BM == 128 || BM == 256, "contiguous tiles cover one or two 128-row blocks");
   static_assert(!SPLIT || MODE == MODE_DENSE, "split-K is for dense GEMMs");
+  static_assert(MODE != MODE_KGROUP || !BF16_OUT, "K-grouped outputs are FP32");
   static_assert(STAGES >= 2, "at least double buffering");
   // Per-wave load instructions per slab (wave 0 issues one more, for the row
   // scales; using the smaller count makes wave 0 wait slightly longer).
@@ -242,6 +271,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int KB = p.k >> 7;
+  const int KQ = (KB + 3) >> 2;  // packed UE8M0 words per row
   const int NBLK = (p.n + 127) >> 7;
   const int tiles_mn = p.tiles_m * p.tiles_n;
   // lane group q reads logical K chunks q and q + 4 (measured free of LDS bank
@@ -256,7 +286,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   for (int tile = vb; tile < p.num_tiles; tile += gridDim.x) {
     int g = 0, t = tile, split = 0;
-    if (MODE == MODE_MASKED) {
+    if (MODE == MODE_MASKED || MODE == MODE_KGROUP) {
       g = t / tiles_mn;
       t -= g * tiles_mn;
     }
@@ -264,8 +294,16 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       split = t / tiles_mn;
       t -= split * tiles_mn;
     }
-    const int kb_begin = SPLIT ? split * p.slabs_per_split : 0;
-    const int kb_end = SPLIT ? min(KB, kb_begin + p.slabs_per_split) : KB;
+    int kb_begin = SPLIT ? split * p.slabs_per_split : 0;
+    int kb_end = SPLIT ? min(KB, kb_begin + p.slabs_per_split) : KB;
+    if (MODE == MODE_KGROUP) {
+      // group g's K blocks start after the blocks of groups 0..g-1; sizes are
+      // device data, so they are clamped into [0, KB] rather than trusted
+      int off = 0;
+      for (int h = 0; h < g; ++h) off += max(p.grp[h], 0) >> 7;
+      kb_begin = min(off, KB);
+      kb_end = min(kb_begin + (max(p.grp[g], 0) >> 7), KB);
+    }
     const int nkb = kb_end - kb_begin;
     int mb, nb;
     raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
@@ -299,10 +337,11 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       bool wave_live = wrow0 < row_end;
       if (MODE == MODE_CONTIG && BM == 256) wave_live = wave_live && (g_half[(wm * TM) >> 7] == g);
 
+      constexpr bool B_GROUPED = MODE == MODE_CONTIG || MODE == MODE_MASKED;
       const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0) + (int64_t)m0 * p.lda;
       const float* SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)g * p.sfa_gs : 0) + m0;
-      const uint8_t* B = p.b + (MODE != MODE_DENSE ? (int64_t)g * p.b_gs : 0) + (int64_t)n0 * p.ldb;
-      const float* SFB = p.sfb + (MODE != MODE_DENSE ? (int64_t)g * p.sfb_gs : 0);
+      const uint8_t* B = p.b + (B_GROUPED ? (int64_t)g * p.b_gs : 0) + (int64_t)n0 * p.ldb;
+      const float* SFB = p.sfb + (B_GROUPED ? (int64_t)g * p.sfb_gs : 0);
       const int64_t a_rows = p.m - m0, b_rows = p.n - n0;
 
       // per-lane offsets of this wave's direct loads (fixed over K)
@@ -316,7 +355,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 
       // scale block of this wave's columns (clamped: columns past N are never stored)
       const int sfb_blk = min((n0 + wn * TN) >> 7, NBLK - 1);
-      const float* SFB_w = SFB + (int64_t)sfb_blk * KB;
+      const float* SFB_w = SFB + (int64_t)sfb_blk * (E8M0 ? KQ : KB);
 
       auto issue_slab = [&](int kb, int stage) {
         uint8_t* base = lds + stage * STAGE;
@@ -328,7 +367,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         for (int i = 0; i < B_LOADS; ++i)
           load_to_lds16(rb, base + A_BYTES + (wave * B_LOADS + i) * 1024, b_off[i]);
         if (wave == 0 && lane < SFA_LANES) {
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA + (int64_t)kb * p.ld_sfa, clamp_bytes(a_rows * 4));
+          const int sf_row = E8M0 ? (kb >> 2) : kb;
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA + (int64_t)sf_row * p.ld_sfa, clamp_bytes(a_rows * 4));
           load_to_lds16(rs, base + A_BYTES + B_BYTES, lane * 16);
         }
       };
@@ -343,17 +383,44 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 #pragma unroll
       for (int i = 0; i < STAGES - 1; ++i)
         if (i < nkb) issue_slab(kb_begin + i, i);
-      float sb_next = nkb > 0 ? load_uniform_f32(SFB_w + kb_begin) : 0.f;
+      // scale of this wave's B block for slab kb (UE8M0: the word holding it)
+      auto sfb_of = [&](int kb) { return load_uniform_f32(SFB_w + (E8M0 ? (kb >> 2) : kb)); };
+      float sb_next = nkb > 0 ? sfb_of(kb_begin) : 0.f;
 
       for (int it = 0; it < nkb; ++it) {
         const int cur = it % STAGES;
         const float sb = sb_next;
         // slabs issued after slab `it` that may stay in flight
         wait_slabs_pending<STAGES - 2, LOADS_PER_SLAB>(min(STAGES - 2, nkb - 1 - it));
-        __syncthreads();  // slab `it` has landed for every wave; stage (it-1) % STAGES is free
+        stage_barrier();  // slab `it` has landed for every wave; stage (it-1) % STAGES is free
         if (it + STAGES - 1 < nkb) issue_slab(kb_begin + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-        if (it + 1 < nkb) sb_next = load_uniform_f32(SFB_w + kb_begin + it + 1);
-        if (wave_live) {
+        if (it + 1 < nkb) sb_next = sfb_of(kb_begin + it + 1);
+        if (wave_live && E8M0) {
+          // UE8M0: scales go into the MFMA, which accumulates across slabs
+          const int sh = 8 * ((kb_begin + it) & 3);
+          const int sbx = (int)(__float_as_uint(sb) >> sh);
+          const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
+          const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
+          const uint32_t* Sw = reinterpret_cast<const uint32_t*>(lds + cur * STAGE + A_BYTES + B_BYTES) + wm * TM + r16;
+          i32x8 fb[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) fb[j] = read_frag(Bs + j * 16 * 128, sw0, sw1);
+          i32x8 fa = read_frag(As, sw0, sw1);
+          int sa = (int)(Sw[0] >> sh);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            i32x8 fa_next = fa;
+            int sa_next = sa;
+            if (i + 1 < FM) {
+              fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
+              sa_next = (int)(Sw[(i + 1) * 16] >> sh);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fa, acc[i][j], sbx, sa);
+            fa = fa_next;
+            sa = sa_next;
+          }
+        } else if (wave_live) {
           const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
           const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
           const float* Ss = reinterpret_cast<const float*>(lds + cur * STAGE + A_BYTES + B_BYTES) + wm * TM + r16;
@@ -397,7 +464,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           }
         }
       }
-      __syncthreads();  // all LDS reads of this tile are done before the next tile's loads
+      stage_barrier();  // all LDS reads of this tile are done before the next tile's loads
 
       if (!wave_live) continue;
       if (SPLIT) {
@@ -422,12 +489,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         bool row_ok = gm < row_end;
         if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
         if (!row_ok) continue;
-        const int64_t drow = (MODE == MODE_MASKED ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+        const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+        const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int gn = n0 + wn * TN + j * 16 + 4 * q4;
           if (gn >= p.n) continue;
-          store_out<BF16_OUT, HAS_C>(p, gm, gn, drow, acc[i][j]);
+          store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
         }
       }
     }
@@ -447,7 +515,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const Params p) {
     const float* W = p.ws + (int64_t)gm * p.ldw + gn;
     f32x4 v = *reinterpret_cast<const f32x4*>(W);
     for (int s = 1; s < p.splits; ++s) v += *reinterpret_cast<const f32x4*>(W + s * split_stride);
-    store_out<BF16_OUT, HAS_C>(p, gm, gn, (int64_t)gm * p.ldd, v);
+    store_out<BF16_OUT, HAS_C>(p, (int64_t)gm * p.ldc, gn, (int64_t)gm * p.ldd, v);
   }
 }
 

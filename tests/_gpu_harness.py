@@ -104,3 +104,20 @@ def take(d: torch.Tensor, rows, cols) -> np.ndarray:
     r = torch.as_tensor(np.asarray(rows), device=d.device, dtype=torch.long)
     c = torch.as_tensor(np.asarray(cols), device=d.device, dtype=torch.long)
     return as_f64(d.index_select(0, r).index_select(1, c))
+
+
+def run_k_grouped(x: dict, with_c: bool = True, in_place: bool = False) -> torch.Tensor:
+    """K-grouped GEMM through the binding; D [G, M, N] FP32 pre-filled with the sentinel."""
+    a, b = fp8_dev(x["a"]), fp8_dev(x["b"])
+    sfa, sfb = to_dev(x["sfa"]), to_dev(x["sfb"])
+    ks = to_dev(x["ks"])
+    g, m, n = x["num_groups"], x["m"], x["n"]
+    if in_place:
+        d = to_dev(x["c"].astype(np.float32))
+        dg.k_grouped_wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d, ks)
+    else:
+        d = out_buffer((g, m), n, "fp32")
+        c = to_dev(x["c"].astype(np.float32)) if with_c else None
+        dg.k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c)
+    torch.cuda.synchronize()
+    return d

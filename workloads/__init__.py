@@ -18,9 +18,13 @@ from .gen import (  # noqa: F401
     quantize_per_block,
     sf_to_mn_major,
     sf_aligned_size,
+    pack_ue8m0,
     gen_dense,
     gen_contiguous,
     gen_masked,
+    gen_k_grouped,
+    gen_quant_input,
+    gen_mqa,
     DENSE_SWEEP,
     workload,
     WORKLOAD_NAMES,
