@@ -132,10 +132,15 @@ def algorithmic_work(x: dict):
     """(flops, bytes) the method must do for one call on inputs ``x``."""
     import numpy as np
     k = x["k"]
-    kb = k // 128
-    out_b = 2 if x["out_dtype"] == "bf16" else 4
+    # scale entries per row along K: FP32 per 128-K block, or packed UE8M0 words
+    kb = _cdiv(k // 128, 4) if x.get("scale_fmt") == "ue8m0" else k // 128
+    out_b = 2 if x.get("out_dtype", "fp32") == "bf16" else 4
     n = x["n"]
     nb = _cdiv(n, 128)
+    if x["kind"] == "k_grouped":
+        m, g = x["m"], x["num_groups"]
+        c_b = g * m * n * 4 if x.get("c") is not None else 0
+        return 2.0 * m * n * k, m * k + n * k + 4 * m * kb + 4 * nb * kb + g * m * n * 4 + c_b
     if x["kind"] == "dense":
         m = x["m"]
         c_b = m * n * out_b if x.get("c") is not None else 0
@@ -171,8 +176,13 @@ class Case:
         a = up(x["a"]).view(torch.float8_e4m3fn)
         b = up(x["b"]).view(torch.float8_e4m3fn)
         sfa, sfb = up(x["sfa"]), up(x["sfb"])
-        dt = torch.bfloat16 if x["out_dtype"] == "bf16" else torch.float32
-        if x["kind"] == "dense":
+        dt = torch.bfloat16 if x.get("out_dtype", "fp32") == "bf16" else torch.float32
+        if x["kind"] == "k_grouped":
+            d = torch.empty(x["num_groups"], x["m"], x["n"], dtype=torch.float32, device=dev)
+            c = up(x["c"]) if x.get("c") is not None else None
+            ks = up(x["ks"])
+            self.call = lambda: dg.k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c)
+        elif x["kind"] == "dense":
             d = torch.empty(x["m"], x["n"], dtype=dt, device=dev)
             c = up(x["c"]).to(dt) if x.get("c") is not None else None
             self.call = lambda: dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c)
@@ -194,7 +204,8 @@ class Case:
 
 
 def time_launches(case: Case, iters: int, flush=None):
-    """Median per-launch time (s) with HIP events on the current stream."""
+    """Median per-launch time (s) with HIP events on the current stream (the
+    stream the library launches on)."""
     import torch
     times = []
     for _ in range(iters):
@@ -225,20 +236,29 @@ def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
         n, k = x["n"], x["k"]
         cols = np.arange(min(n, budget_cols))
         t0 = time.perf_counter()
-        if x["kind"] == "dense":
+        ue = x.get("scale_fmt") == "ue8m0"
+        kk = k
+        if x["kind"] == "k_grouped":
+            rows = np.arange(min(x["m"], budget_rows // 4))
+            oracle.ref_k_grouped(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], x.get("c"), rows=rows, cols=cols)
+            nrows = len(rows)
+        elif x["kind"] == "dense":
             rows = np.arange(min(x["m"], budget_rows))
-            oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"), rows=rows, cols=cols)
+            ref = oracle.ref_dense_ue8m0 if ue else oracle.ref_dense
+            ref(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"), rows=rows, cols=cols)
             nrows = len(rows)
         elif x["kind"] == "contiguous":
             valid = np.nonzero(x["m_indices"] >= 0)[0][:budget_rows]
-            oracle.ref_contiguous(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"], rows=valid, cols=cols)
+            ref = oracle.ref_contiguous_ue8m0 if ue else oracle.ref_contiguous
+            ref(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"], rows=valid, cols=cols)
             nrows = len(valid)
         else:
             groups = np.arange(min(x["num_groups"], 2))
-            oracle.ref_masked(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
+            ref = oracle.ref_masked_ue8m0 if ue else oracle.ref_masked
+            ref(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
             nrows = int(np.clip(x["masked_m"][groups], 0, x["m_max"]).sum())
         total_s += time.perf_counter() - t0
-        total_flops += 2.0 * nrows * len(cols) * k
+        total_flops += 2.0 * nrows * len(cols) * kk
     return dict(value=total_flops / total_s / 1e12, unit="TFLOPS", cores=int(threads), kind="oracle",
                 sample=f"first {budget_rows} valid rows x first {budget_cols} columns of every case "
                        f"(masked: first 2 groups), FP64 numpy, {total_flops / 1e9:.1f} GFLOP in {total_s:.1f} s",
@@ -294,7 +314,9 @@ def main():
         print(f"bench:   {c.label}: {c.flops / 1e9:.1f} GFLOP, {c.bytes / 1e6:.1f} MB, {c.bound}-bound",
               file=sys.stderr, flush=True)
 
-    # per-launch timing, warm (back to back) and cold (after a cache flush)
+    # per-launch timing, warm (back to back) and cold (after a cache flush).
+    # Cold is the kernel's own time: the flush keeps the GPU busy while the
+    # host enqueues the launch, so no host gap lands between the events.
     # read-only flush: evicts the operands from L2 and the Infinity Cache without
     # leaving dirty lines whose write-back would overlap the timed launch
     flush_buf = torch.ones(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
@@ -314,7 +336,7 @@ def main():
     del flush_buf
     dom = max(range(len(cases)), key=lambda i: cases[i].warm_s)
 
-    # the timed steps
+    # the timed steps (the dominant case bracketed by HIP events on the launch stream)
     for _ in range(args.warmup):
         for c in cases:
             c.call()
@@ -363,9 +385,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate",
-        "data": "synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 FP32 scales)",
+        "data": "synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 "
+                + ("UE8M0 power-of-two" if cases[0].x.get("scale_fmt") == "ue8m0" else "FP32") + " scales)",
         "config": {"workload": args.workload, "cases": [c.label for c in cases],
-                   "out_dtype": cases[0].x["out_dtype"], "pct_of_fp8_peak": 100.0 * value / PEAK_FP8_TFLOPS},
+                   "out_dtype": cases[0].x.get("out_dtype", "fp32"),
+                   "pct_of_fp8_peak": 100.0 * value / PEAK_FP8_TFLOPS},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,

@@ -135,3 +135,63 @@ def test_binding_refuses_cpu_tensors(lib):
     d = torch.zeros(128, 128, dtype=torch.bfloat16)
     with pytest.raises((TypeError, ValueError)):
         dg.fp8_gemm_nt((a, s), (a, s), d)
+
+
+def test_header_declares_next_entry_points():
+    names = _declared_functions()
+    for want in ("dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+                 "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_k_grouped_fp8_gemm_nt_contiguous",
+                 "dg_wgrad_fp8_gemm_nt", "dg_k_grouped_wgrad_fp8_gemm_nt"):
+        assert want in names
+
+
+def test_ue8m0_validation(lib):
+    f = lib.dg_fp8_gemm_nt_ue8m0
+    ok = (P, 512, P, 128, P, 512, P, None, 0, P, 256, 0, 128, 256, 512, None)
+    bad_ld = list(ok)
+    bad_ld[3] = 130  # ld_sfa not a multiple of 4 words
+    assert f(*bad_ld) == INVALID
+    bad_k = list(ok)
+    bad_k[14] = 500
+    assert f(*bad_k) == UNSUPPORTED
+    empty = list(ok)
+    empty[12] = 0
+    assert f(*empty) == 0
+    g = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0
+    assert g(P, P, 256, P, P, P, 0, None, 256, 256, 512, 4, None) == INVALID  # no m_indices
+    h = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0
+    assert h(P, P, 100, P, P, P, 0, P, 4, 256, 256, 512, 0, None) == INVALID  # ld_sfa < m_max
+
+
+def _kg(lib, **kw):
+    args = dict(a=P, sfa=P, ld_sfa=256, b=P, sfb=P, c=None, d=P, ks=P, g=4, m=256, n=256, k=1024)
+    args.update(kw)
+    return lib.dg_k_grouped_fp8_gemm_nt_contiguous(args["a"], args["sfa"], args["ld_sfa"], args["b"], args["sfb"],
+                                                   args["c"], args["d"], args["ks"], args["g"], args["m"],
+                                                   args["n"], args["k"], None)
+
+
+def test_k_grouped_and_wgrad_validation(lib):
+    assert _kg(lib, k=1000) == UNSUPPORTED
+    assert _kg(lib, g=-1) == INVALID
+    assert _kg(lib, ks=None) == INVALID
+    assert _kg(lib, ks=P + 2) == INVALID
+    assert _kg(lib, c=P + 4) == INVALID
+    assert _kg(lib, n=3) == INVALID    # FP32 rows of 12 bytes
+    assert _kg(lib, ld_sfa=100) == INVALID
+    assert _kg(lib, m=0) == 0 and _kg(lib, g=0) == 0
+    w = lib.dg_wgrad_fp8_gemm_nt
+    assert w(P, 512, P, 128, P, 512, P, P, 100, 128, 256, 512, None) == INVALID  # ldd < n
+    assert w(P, 512, P, 128, P, 512, P, P, 256, 0, 256, 512, None) == 0
+    kw = lib.dg_k_grouped_wgrad_fp8_gemm_nt
+    assert kw(P, P, 256, P, P, P, None, 4, 256, 256, 1024, None) == INVALID  # no ks
+
+
+def test_binding_leading_dimension_of_size_one_dims():
+    import torch
+    from moe_grouped_gemm_tiles_amd import _ld
+    t = torch.zeros(1, 4, dtype=torch.int32).as_strided((1, 4), (1, 1))  # any stride is legal for a size-1 dim
+    assert _ld(t, 0, 4) == 4
+    assert _ld(torch.zeros(1, 6), 0, 4) == 8
+    assert _ld(torch.zeros(3, 1, 5), 1, 4) == 8
+    assert _ld(torch.zeros(5, 7)[:, :3], 0, 4) == 7

@@ -316,7 +316,8 @@ DENSE_SWEEP_NK = [(2112, 7168), (24576, 1536), (7168, 16384), (4096, 7168), (716
 DENSE_SWEEP_M = [64, 128, 4096]
 DENSE_SWEEP = [(m, n, k) for m in DENSE_SWEEP_M for (n, k) in DENSE_SWEEP_NK]
 
-WORKLOAD_NAMES = ("dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc")
+WORKLOAD_NAMES = ("dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc",
+                  "dense_sweep_ue8m0", "contiguous_moe_ue8m0", "masked_decode_ue8m0", "k_grouped_wgrad")
 
 
 def workload(name: str):
@@ -343,6 +344,26 @@ def workload(name: str):
                             num_groups=16, m_max=256,
                             gen=(lambda n=n, k=k, j=j: gen_masked(16, 256, n, k, seed=30 + j))))
         return out
+    if name == "dense_sweep_ue8m0":
+        out = []
+        for i, (m, n, k) in enumerate(DENSE_SWEEP):
+            out.append(dict(label=f"dense ue8m0 M={m} N={n} K={k}", kind="dense", m=m, n=n, k=k,
+                            gen=(lambda m=m, n=n, k=k, i=i: gen_dense(m, n, k, seed=100 + i, scale_fmt="ue8m0"))))
+        return out
+    if name == "contiguous_moe_ue8m0":
+        return [dict(label="contiguous ue8m0 G=8 N=4096 K=7168", kind="contiguous", n=4096, k=7168, num_groups=8,
+                     gen=lambda: gen_contiguous(8, 4096, 7168, seed=2, scale_fmt="ue8m0"))]
+    if name == "masked_decode_ue8m0":
+        out = []
+        for j, (n, k) in enumerate([(4096, 7168), (7168, 2048)]):
+            out.append(dict(label=f"masked ue8m0 G=16 Mmax=256 N={n} K={k}", kind="masked", n=n, k=k,
+                            num_groups=16, m_max=256,
+                            gen=(lambda n=n, k=k, j=j: gen_masked(16, 256, n, k, seed=30 + j, scale_fmt="ue8m0"))))
+        return out
+    if name == "k_grouped_wgrad":
+        # weight gradient of the contiguous MoE layer: dW[g] [4096, 7168] over each expert's tokens
+        return [dict(label="k-grouped wgrad G=8 M=4096 N=7168 K_g~U[1,8192]", kind="k_grouped", m=4096, n=7168,
+                     num_groups=8, gen=lambda: gen_k_grouped(8, 4096, 7168, seed=5))]
     if name == "dense_long_k_acc":
         return [dict(label="dense+C M=8192 N=8192 K=16384 fp32", kind="dense", m=8192, n=8192, k=16384,
                      gen=lambda: gen_dense(8192, 8192, 16384, seed=4, with_c=True, out_dtype="fp32"))]
