@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (no sparsity)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
-KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_tiles_amd", "csrc", f) for f in ("dg_kernels.hpp", "dg_api.hip")]
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_tiles_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_CAL_MB = 256  # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
@@ -131,6 +132,11 @@ def _cdiv(a, b):
 def algorithmic_work(x: dict):
     """(flops, bytes) the method must do for one call on inputs ``x``."""
     import numpy as np
+    if x["kind"] in ("quant_token", "quant_block"):
+        m, k = x["m"], x["k"]
+        es = 2 if x["dtype"] == "bf16" else 4
+        scales = m * (k // 128) * 4 if x["kind"] == "quant_token" else _cdiv(m, 128) * (k // 128) * 4
+        return 0.0, m * k * es + m * k + scales
     k = x["k"]
     # scale entries per row along K: FP32 per 128-K block, or packed UE8M0 words
     kb = _cdiv(k // 128, 4) if x.get("scale_fmt") == "ue8m0" else k // 128
@@ -172,6 +178,21 @@ class Case:
 
         def up(v):
             return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+        if x["kind"] in ("quant_token", "quant_block"):
+            xin = up(x["x"]).to(torch.bfloat16 if x["dtype"] == "bf16" else torch.float32)
+            m, k = x["m"], x["k"]
+            q = torch.empty(m, k, dtype=torch.uint8, device=dev)
+            if x["kind"] == "quant_token":
+                sf = torch.empty(k // 128, _cdiv(m, 4) * 4, dtype=torch.float32, device=dev)
+                self.call = lambda: dg.per_token_cast_to_fp8(xin, q, sf)
+            else:
+                sf = torch.empty(_cdiv(m, 128), k // 128, dtype=torch.float32, device=dev)
+                self.call = lambda: dg.per_block_cast_to_fp8(xin, q, sf)
+            self.d = q
+            self.bound = "hbm"
+            self.roof_s = self.bytes / (PEAK_HBM_GBS * 1e9)
+            return
 
         a = up(x["a"]).view(torch.float8_e4m3fn)
         b = up(x["b"]).view(torch.float8_e4m3fn)
@@ -231,11 +252,20 @@ def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    total_flops, total_s = 0.0, 0.0
+    total_flops, total_bytes, total_s = 0.0, 0.0, 0.0
     for x in inputs:
-        n, k = x["n"], x["k"]
-        cols = np.arange(min(n, budget_cols))
+        k = x["k"]
         t0 = time.perf_counter()
+        if x["kind"] not in ("quant_token", "quant_block"):
+            n = x["n"]
+            cols = np.arange(min(n, budget_cols))
+        if x["kind"] in ("quant_token", "quant_block"):
+            nrows = min(x["m"], budget_rows)
+            xs = x["x"][:nrows]
+            (oracle.quant_per_token if x["kind"] == "quant_token" else oracle.quant_per_block)(xs)
+            total_s += time.perf_counter() - t0
+            total_bytes += nrows * k * (2 if x["dtype"] == "bf16" else 4) + nrows * k
+            continue
         ue = x.get("scale_fmt") == "ue8m0"
         kk = k
         if x["kind"] == "k_grouped":
@@ -259,6 +289,11 @@ def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
             nrows = int(np.clip(x["masked_m"][groups], 0, x["m_max"]).sum())
         total_s += time.perf_counter() - t0
         total_flops += 2.0 * nrows * len(cols) * kk
+    if total_flops == 0:
+        return dict(value=total_bytes / total_s / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                    sample=f"first {budget_rows} rows of every case, numpy FP32 cast, "
+                           f"{total_bytes / 1e6:.1f} MB in {total_s:.1f} s",
+                    host_cpus=len(os.sched_getaffinity(0)))
     return dict(value=total_flops / total_s / 1e12, unit="TFLOPS", cores=int(threads), kind="oracle",
                 sample=f"first {budget_rows} valid rows x first {budget_cols} columns of every case "
                        f"(masked: first 2 groups), FP64 numpy, {total_flops / 1e9:.1f} GFLOP in {total_s:.1f} s",
@@ -356,7 +391,13 @@ def main():
     elapsed = t1 - t0
     dom_s = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / args.steps
     step_flops = sum(c.flops for c in cases)
-    value = step_flops * args.steps / elapsed / 1e12
+    step_bytes = sum(c.bytes for c in cases)
+    if step_flops > 0:
+        metric = "FP8 scaled-GEMM TFLOPS and % of MI355X dense-FP8 peak (dense, grouped)"
+        value, unit = step_flops * args.steps / elapsed / 1e12, "TFLOPS"
+    else:
+        metric = "FP8 cast throughput, GB/s of algorithmic HBM traffic (read input + write codes and scales)"
+        value, unit = step_bytes * args.steps / elapsed / 1e9, "GB/s"
 
     dc = cases[dom]
     if dc.bound == "mfma":
@@ -374,9 +415,9 @@ def main():
         cpu = cpu_baseline([c.x for c in cases])
 
     out = {
-        "metric": "FP8 scaled-GEMM TFLOPS and % of MI355X dense-FP8 peak (dense, grouped)",
+        "metric": metric,
         "value": value,
-        "unit": "TFLOPS",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -384,16 +425,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate",
-        "data": "synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 "
-                + ("UE8M0 power-of-two" if cases[0].x.get("scale_fmt") == "ue8m0" else "FP32") + " scales)",
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate" if step_flops > 0 else "bf16 -> fp8_e4m3 + fp32 scales",
+        "data": ("synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 "
+                 + ("UE8M0 power-of-two" if cases[0].x.get("scale_fmt") == "ue8m0" else "FP32") + " scales)")
+                if step_flops > 0 else "synthetic (seeded N(0,1) rows with e^U(-4,4) magnitude spread, BF16)",
         "config": {"workload": args.workload, "cases": [c.label for c in cases],
-                   "out_dtype": cases[0].x.get("out_dtype", "fp32"),
-                   "pct_of_fp8_peak": 100.0 * value / PEAK_FP8_TFLOPS},
+                   "out_dtype": cases[0].x.get("out_dtype", "fp32")},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
     }
+    if step_flops > 0:
+        out["config"]["pct_of_fp8_peak"] = 100.0 * value / PEAK_FP8_TFLOPS
     print(json.dumps(out), flush=True)
 
 

@@ -212,6 +212,36 @@ dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_
                                          const void* b, const float* sfb, float* d, const int32_t* ks,
                                          int num_groups, int m, int n, int k_total, hipStream_t stream);
 
+/*
+ * FP8 quantization of GEMM operands (the cast the GEMM's caller performs,
+ * [README] "Interfaces > Notices": FP8 casting and transposition are the
+ * caller's job, and the LHS scale factors must be transposed and aligned;
+ * "Utilities": helpers producing those scale layouts, FP32 or packed UE8M0).
+ *
+ * Scale rule: FP32 s = amax / 448 (computed in FP32; 1 for an all-zero
+ * block); UE8M0 s = the smallest power of two >= fp32(amax / 448) (1 for an
+ * all-zero block), stored as the byte log2(s) + 127.  Codes are
+ * E4M3(clamp(x / s, -448, 448)): the quotient correctly rounded to FP32, then
+ * rounded to E4M3 with ties to even.  Inputs must be finite (codes of NaN or
+ * Inf inputs are unspecified).
+ *
+ * dg_per_token_cast_to_fp8: x [m, k] (BF16 or FP32, row stride ldx elements,
+ *   16-B aligned rows) -> q E4M3 [m, k] (row stride ldq bytes, ldq % 8 == 0)
+ *   and sf, one scale per (row, 128-K block), stored transposed: FP32
+ *   [k/128][ld_sf] or (ue8m0 != 0) int32 words [ceil(k/512)][ld_sf], four
+ *   bytes per word along K (padding bytes 127); ld_sf >= m, ld_sf % 4 == 0,
+ *   sf 16-B aligned.  Columns m..ld_sf-1 of sf are not written.  This is the
+ *   sfa operand of the GEMM entry points.
+ * dg_per_block_cast_to_fp8: w [n, k] -> q [n, k] and sf, one scale per
+ *   128 x 128 block: FP32 [ceil(n/128)][k/128] or int32 words
+ *   [ceil(n/128)][ceil(k/512)] (padding bytes 127).  This is the sfb operand.
+ * k % 128 != 0 -> DG_ERROR_NOT_SUPPORTED; m (n) == 0 or k == 0 -> DG_SUCCESS.
+ */
+dg_status dg_per_token_cast_to_fp8(const void* x, int64_t ldx, dg_dtype x_dtype, void* q, int64_t ldq,
+                                   void* sf, int64_t ld_sf, int ue8m0, int m, int k, hipStream_t stream);
+dg_status dg_per_block_cast_to_fp8(const void* w, int64_t ldw, dg_dtype w_dtype, void* q, int64_t ldq,
+                                   void* sf, int ue8m0, int n, int k, hipStream_t stream);
+
 /* Row (M-grouped) and K (K-grouped) alignment of group segments in the
  * contiguous layouts (128).
  * [README] "Utilities": get_mk_alignment_for_contiguous_layout. */

@@ -13,6 +13,8 @@ as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
 * ``k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c=None)``
 * ``wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d)`` and
   ``k_grouped_wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d, ks)`` (D += ..., FP32)
+* ``per_token_cast_to_fp8(x, q, sf)`` and ``per_block_cast_to_fp8(w, q, sf)``
+  (the caller's FP8 cast, writing the scale layouts the GEMMs take)
 * ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
   ``set_num_cus(n)`` / ``get_num_cus()``
 
@@ -45,6 +47,8 @@ __all__ = [
     "k_grouped_fp8_gemm_nt_contiguous",
     "wgrad_fp8_gemm_nt",
     "k_grouped_wgrad_fp8_gemm_nt",
+    "per_token_cast_to_fp8",
+    "per_block_cast_to_fp8",
     "get_mk_alignment_for_contiguous_layout",
     "get_sf_aligned_size",
     "set_num_cus",
@@ -81,6 +85,8 @@ _SIGNATURES = {
                                                    _i32, _i32, _i32, _i32, _vp]),
     "dg_wgrad_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "dg_k_grouped_wgrad_fp8_gemm_nt": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "dg_per_token_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "dg_per_block_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _vp]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
@@ -345,6 +351,46 @@ def k_grouped_wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, ks: torch.Tenso
                                             sfb.data_ptr(), d.data_ptr(), ks.data_ptr(), g, m, n, k, _stream(d))
     _check(st)
     return d
+
+
+def _cast_args(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor):
+    if x.dtype not in _DTYPES or not x.is_cuda or x.dim() != 2 or not _unit_last_stride(x):
+        raise TypeError("x must be a 2-D bfloat16 or float32 GPU tensor, contiguous in its last dimension")
+    _fp8(q, "q")
+    if q.shape != x.shape:
+        raise ValueError("q must have x's shape")
+    if sf.dtype not in (torch.float32, torch.int32) or not sf.is_cuda or not _unit_last_stride(sf):
+        raise TypeError("sf must be a float32 (FP32 scales) or int32 (packed UE8M0) GPU tensor")
+    return _DTYPES[x.dtype], sf.dtype == torch.int32
+
+
+def per_token_cast_to_fp8(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor):
+    """Per-(row, 128-K) FP8 cast of x [M, K] into q [M, K] and the transposed scales sf:
+    FP32 [K/128, ld >= M] or packed UE8M0 int32 [ceil(K/512), ld >= M]."""
+    lib = load_library()
+    dt, ue = _cast_args(x, q, sf)
+    m, k = x.shape
+    if sf.dim() != 2 or sf.shape[0] != _sf_rows(k, ue) or sf.shape[1] < m:
+        raise ValueError(f"sf shape {tuple(sf.shape)} does not fit x {tuple(x.shape)}")
+    st = lib.dg_per_token_cast_to_fp8(x.data_ptr(), _ld(x, 0, 16 // x.element_size()), dt, q.data_ptr(),
+                                      _ld(q, 0, 8), sf.data_ptr(), _ld(sf, 0, 4), int(ue), m, k, _stream(x))
+    _check(st)
+    return q, sf
+
+
+def per_block_cast_to_fp8(w: torch.Tensor, q: torch.Tensor, sf: torch.Tensor):
+    """Per-128x128-block FP8 cast of w [N, K] into q [N, K] and sf: FP32 [ceil(N/128), K/128]
+    or packed UE8M0 int32 [ceil(N/128), ceil(K/512)]."""
+    lib = load_library()
+    dt, ue = _cast_args(w, q, sf)
+    n, k = w.shape
+    _dense_contig(sf, "sf")
+    if sf.shape != ((n + 127) // 128, _sf_rows(k, ue)):
+        raise ValueError(f"sf shape {tuple(sf.shape)} does not fit w {tuple(w.shape)}")
+    st = lib.dg_per_block_cast_to_fp8(w.data_ptr(), _ld(w, 0, 16 // w.element_size()), dt, q.data_ptr(),
+                                      _ld(q, 0, 8), sf.data_ptr(), int(ue), n, k, _stream(w))
+    _check(st)
+    return q, sf
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

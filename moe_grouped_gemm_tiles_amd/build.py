@@ -24,8 +24,8 @@ LIB = os.path.join(PKG, "libdg.so")
 RES = os.path.join(PKG, "libdg.resources.txt")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "dg_api.hip")]
-HEADERS = [os.path.join(CSRC, "dg_kernels.hpp"), os.path.join(INCLUDE, "dg.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("dg_api.hip", "dg_quant.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("dg_kernels.hpp", "dg_common.hpp")] + [os.path.join(INCLUDE, "dg.h")]
 
 
 def hipcc() -> str:

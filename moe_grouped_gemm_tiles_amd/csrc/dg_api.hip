@@ -19,6 +19,7 @@
 #include <utility>
 
 #include "dg.h"
+#include "dg_common.hpp"
 #include "dg_kernels.hpp"
 
 namespace {
@@ -26,7 +27,6 @@ namespace {
 constexpr int kAlignM = 128;
 constexpr int kMaxDevices = 64;
 
-thread_local char g_last_hip_error[256] = "";
 
 std::atomic<int> g_num_cus{-1};  // -1: not yet read from the environment
 int g_device_cus[kMaxDevices] = {0};
@@ -47,10 +47,7 @@ void read_env() {
   });
 }
 
-dg_status hip_fail(hipError_t e) {
-  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
-  return DG_ERROR_LAUNCH_FAILED;
-}
+dg_status hip_fail(hipError_t e) { return dg::record_hip_error(e); }
 
 // CUs the kernels may spread over on the current device.
 dg_status usable_cus(int* out) {
@@ -427,6 +424,17 @@ dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const 
 
 }  // namespace
 
+namespace dg {
+
+thread_local char g_last_hip_error[256] = "";
+
+dg_status record_hip_error(hipError_t e) {
+  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
+  return DG_ERROR_LAUNCH_FAILED;
+}
+
+}  // namespace dg
+
 extern "C" {
 
 dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
@@ -516,6 +524,6 @@ const char* dg_status_string(dg_status s) {
   return "DG_UNKNOWN_STATUS";
 }
 
-const char* dg_last_hip_error(void) { return g_last_hip_error; }
+const char* dg_last_hip_error(void) { return dg::g_last_hip_error; }
 
 }  // extern "C"

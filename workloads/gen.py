@@ -317,7 +317,8 @@ DENSE_SWEEP_M = [64, 128, 4096]
 DENSE_SWEEP = [(m, n, k) for m in DENSE_SWEEP_M for (n, k) in DENSE_SWEEP_NK]
 
 WORKLOAD_NAMES = ("dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc",
-                  "dense_sweep_ue8m0", "contiguous_moe_ue8m0", "masked_decode_ue8m0", "k_grouped_wgrad")
+                  "dense_sweep_ue8m0", "contiguous_moe_ue8m0", "masked_decode_ue8m0", "k_grouped_wgrad",
+                  "quant_moe")
 
 
 def workload(name: str):
@@ -364,6 +365,15 @@ def workload(name: str):
         # weight gradient of the contiguous MoE layer: dW[g] [4096, 7168] over each expert's tokens
         return [dict(label="k-grouped wgrad G=8 M=4096 N=7168 K_g~U[1,8192]", kind="k_grouped", m=4096, n=7168,
                      num_groups=8, gen=lambda: gen_k_grouped(8, 4096, 7168, seed=5))]
+    if name == "quant_moe":
+        # the casts feeding the contiguous MoE GEMM: token activations (1x128
+        # scales, transposed) and the 8 experts' weights (128x128 scales), BF16 in
+        return [dict(label="per-token cast BF16 [33280, 7168]", kind="quant_token", m=33280, k=7168,
+                     gen=lambda: dict(kind="quant_token", m=33280, k=7168, dtype="bf16",
+                                      x=gen_quant_input(33280, 7168, seed=6))),
+                dict(label="per-block cast BF16 [32768, 7168]", kind="quant_block", m=32768, k=7168,
+                     gen=lambda: dict(kind="quant_block", m=32768, k=7168, dtype="bf16",
+                                      x=gen_quant_input(32768, 7168, seed=7)))]
     if name == "dense_long_k_acc":
         return [dict(label="dense+C M=8192 N=8192 K=16384 fp32", kind="dense", m=8192, n=8192, k=16384,
                      gen=lambda: gen_dense(8192, 8192, 16384, seed=4, with_c=True, out_dtype="fp32"))]
