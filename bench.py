@@ -132,6 +132,13 @@ def _cdiv(a, b):
 def algorithmic_work(x: dict):
     """(flops, bytes) the method must do for one call on inputs ``x``."""
     import numpy as np
+    if x["kind"] == "mqa":
+        lo = np.clip(x["ks"], 0, x["s_kv"])
+        hi = np.clip(x["ke"], 0, x["s_kv"])
+        pairs = float(np.maximum(hi - lo, 0).sum())
+        s, h, d, s_kv = x["s"], x["h"], x["d"], x["s_kv"]
+        # q, kv, scales, weights, ranges in; every logit out (clean_logits fills -inf)
+        return 2.0 * h * d * pairs, s * h * d + s_kv * d + 4 * s_kv + 4 * s * h + 8 * s + 4 * s * s_kv
     if x["kind"] in ("quant_token", "quant_block"):
         m, k = x["m"], x["k"]
         es = 2 if x["dtype"] == "bf16" else 4
@@ -179,6 +186,18 @@ class Case:
         def up(v):
             return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
 
+        if x["kind"] == "mqa":
+            q = up(x["q"]).view(torch.float8_e4m3fn)
+            kv = up(x["kv"]).view(torch.float8_e4m3fn)
+            sf, w, ks, ke = up(x["sf"]), up(x["w"]), up(x["ks"]), up(x["ke"])
+            out = torch.empty(x["s"], x["s_kv"], dtype=torch.float32, device=dev)
+            self.call = lambda: dg.fp8_mqa_logits(q, (kv, sf), w, ks, ke, True, out)
+            self.d = out
+            rt_mfma = self.flops / (PEAK_FP8_TFLOPS * 1e12)
+            rt_hbm = self.bytes / (PEAK_HBM_GBS * 1e9)
+            self.bound = "mfma" if rt_mfma >= rt_hbm else "hbm"
+            self.roof_s = max(rt_mfma, rt_hbm)
+            return
         if x["kind"] in ("quant_token", "quant_block"):
             xin = up(x["x"]).to(torch.bfloat16 if x["dtype"] == "bf16" else torch.float32)
             m, k = x["m"], x["k"]
@@ -256,9 +275,17 @@ def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
     for x in inputs:
         k = x["k"]
         t0 = time.perf_counter()
-        if x["kind"] not in ("quant_token", "quant_block"):
+        if x["kind"] not in ("quant_token", "quant_block", "mqa"):
             n = x["n"]
             cols = np.arange(min(n, budget_cols))
+        if x["kind"] == "mqa":
+            rows = np.arange(0, x["s"], max(1, x["s"] // 64))
+            oracle.ref_mqa_logits(x["q"], x["kv"], x["sf"], x["w"], x["ks"], x["ke"], True, rows=rows)
+            total_s += time.perf_counter() - t0
+            lo = np.clip(x["ks"][rows], 0, x["s_kv"])
+            hi = np.clip(x["ke"][rows], 0, x["s_kv"])
+            total_flops += 2.0 * x["h"] * x["d"] * float(np.maximum(hi - lo, 0).sum())
+            continue
         if x["kind"] in ("quant_token", "quant_block"):
             nrows = min(x["m"], budget_rows)
             xs = x["x"][:nrows]
@@ -392,7 +419,10 @@ def main():
     dom_s = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / args.steps
     step_flops = sum(c.flops for c in cases)
     step_bytes = sum(c.bytes for c in cases)
-    if step_flops > 0:
+    if step_flops > 0 and cases[0].x["kind"] == "mqa":
+        metric = "FP8 MQA-logits TFLOPS (2*H*D per valid query-key pair) and % of MI355X dense-FP8 peak"
+        value, unit = step_flops * args.steps / elapsed / 1e12, "TFLOPS"
+    elif step_flops > 0:
         metric = "FP8 scaled-GEMM TFLOPS and % of MI355X dense-FP8 peak (dense, grouped)"
         value, unit = step_flops * args.steps / elapsed / 1e12, "TFLOPS"
     else:
@@ -426,7 +456,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate" if step_flops > 0 else "bf16 -> fp8_e4m3 + fp32 scales",
-        "data": ("synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 "
+        "data": "synthetic (seeded N(0,1) q and kv cast to E4M3, kv scaled per row by amax/448, "
+                "weights N(0,1)/sqrt(H), causal ranges)" if cases[0].x["kind"] == "mqa" else
+                ("synthetic (seeded N(0,1), quantized to E4M3 with 1x128 / 128x128 "
                  + ("UE8M0 power-of-two" if cases[0].x.get("scale_fmt") == "ue8m0" else "FP32") + " scales)")
                 if step_flops > 0 else "synthetic (seeded N(0,1) rows with e^U(-4,4) magnitude spread, BF16)",
         "config": {"workload": args.workload, "cases": [c.label for c in cases],

@@ -242,6 +242,30 @@ dg_status dg_per_token_cast_to_fp8(const void* x, int64_t ldx, dg_dtype x_dtype,
 dg_status dg_per_block_cast_to_fp8(const void* w, int64_t ldw, dg_dtype w_dtype, void* q, int64_t ldq,
                                    void* sf, int ue8m0, int n, int k, hipStream_t stream);
 
+/*
+ * Weighted-ReLU MQA logits (the lightning-indexer scoring kernel, non-paged).
+ *   [README] "V3.2 MQA kernels for the indexer": for query i and each key j
+ *   in [ks[i], ke[i]),
+ *     out[i, j] = sum_h weights[i, h] * relu( q[i, h, :] . kv[j, :] * kv_sf[j] ),
+ *   positions outside the range are set to -inf when clean_logits != 0.
+ *
+ * q        E4M3 [s, num_heads, head_dim] contiguous, 16-B aligned (no scale).
+ * kv       E4M3 [s_kv, head_dim] contiguous, 16-B aligned.
+ * kv_sf    FP32 [s_kv], one scale per kv row; must be >= 0 (a quantization
+ *          scale; the kernel applies it after the ReLU).
+ * weights  FP32 [s, num_heads] contiguous, 16-B aligned.
+ * ks, ke   DEVICE int32 [s]: key range of each query, clamped to [0, s_kv];
+ *          an empty range writes no logit.
+ * out      FP32 [s, ld_out], ld_out >= s_kv.  Without clean_logits the
+ *          positions outside each range are left untouched.
+ * head_dim must be 128 and num_heads a multiple of 16 up to 64
+ * (else DG_ERROR_NOT_SUPPORTED); s == 0 or s_kv == 0 -> DG_SUCCESS.
+ */
+dg_status dg_fp8_mqa_logits(const void* q, const void* kv, const float* kv_sf, const float* weights,
+                            const int32_t* ks, const int32_t* ke, float* out, int64_t ld_out,
+                            int s, int s_kv, int num_heads, int head_dim, int clean_logits,
+                            hipStream_t stream);
+
 /* Row (M-grouped) and K (K-grouped) alignment of group segments in the
  * contiguous layouts (128).
  * [README] "Utilities": get_mk_alignment_for_contiguous_layout. */

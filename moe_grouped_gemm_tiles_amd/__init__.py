@@ -15,6 +15,8 @@ as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
   ``k_grouped_wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d, ks)`` (D += ..., FP32)
 * ``per_token_cast_to_fp8(x, q, sf)`` and ``per_block_cast_to_fp8(w, q, sf)``
   (the caller's FP8 cast, writing the scale layouts the GEMMs take)
+* ``fp8_mqa_logits(q, (kv, kv_sf), weights, ks, ke, clean_logits, out)``
+  (README "V3.2 MQA kernels for the indexer")
 * ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
   ``set_num_cus(n)`` / ``get_num_cus()``
 
@@ -49,6 +51,7 @@ __all__ = [
     "k_grouped_wgrad_fp8_gemm_nt",
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
+    "fp8_mqa_logits",
     "get_mk_alignment_for_contiguous_layout",
     "get_sf_aligned_size",
     "set_num_cus",
@@ -87,6 +90,7 @@ _SIGNATURES = {
     "dg_k_grouped_wgrad_fp8_gemm_nt": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "dg_per_token_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp]),
     "dg_per_block_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _vp]),
+    "dg_fp8_mqa_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
@@ -391,6 +395,35 @@ def per_block_cast_to_fp8(w: torch.Tensor, q: torch.Tensor, sf: torch.Tensor):
                                       _ld(q, 0, 8), sf.data_ptr(), int(ue), n, k, _stream(w))
     _check(st)
     return q, sf
+
+
+def fp8_mqa_logits(q: torch.Tensor, kv_pair, weights: torch.Tensor, ks: torch.Tensor, ke: torch.Tensor,
+                   clean_logits: bool, out: torch.Tensor):
+    """Weighted-ReLU MQA logits: q E4M3 [S, H, D], kv (E4M3 [S_kv, D], FP32 scales [S_kv]),
+    weights FP32 [S, H], key ranges ks/ke int32 [S] -> out FP32 [S, S_kv] (caller-allocated)."""
+    lib = load_library()
+    kv, kv_sf = kv_pair
+    for t, nm in ((q, "q"), (kv, "kv"), (kv_sf, "kv_sf"), (weights, "weights"), (ks, "ks"), (ke, "ke")):
+        _dense_contig(t, nm)
+    _fp8(q, "q")
+    _fp8(kv, "kv")
+    _f32(kv_sf, "kv_sf")
+    _f32(weights, "weights")
+    if out.dtype != torch.float32 or not out.is_cuda or not _unit_last_stride(out):
+        raise TypeError("out must be a float32 GPU tensor, contiguous in its last dimension")
+    for t, nm in ((ks, "ks"), (ke, "ke")):
+        if t.dtype != torch.int32 or not t.is_cuda:
+            raise TypeError(f"{nm} must be an int32 GPU tensor")
+    s, h, d = q.shape
+    s_kv = kv.shape[0]
+    if kv.shape != (s_kv, d) or kv_sf.shape != (s_kv,) or weights.shape != (s, h) or ks.shape != (s,) \
+            or ke.shape != (s,) or out.shape != (s, s_kv):
+        raise ValueError("shape mismatch")
+    st = lib.dg_fp8_mqa_logits(q.data_ptr(), kv.data_ptr(), kv_sf.data_ptr(), weights.data_ptr(), ks.data_ptr(),
+                               ke.data_ptr(), out.data_ptr(), _ld(out, 0, 1), s, s_kv, h, d, int(bool(clean_logits)),
+                               _stream(out))
+    _check(st)
+    return out
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

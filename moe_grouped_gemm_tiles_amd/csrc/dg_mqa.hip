@@ -1,0 +1,229 @@
+// dg_mqa.hip -- weighted-ReLU MQA logits (the lightning-indexer scoring
+// kernel) on gfx950.
+//
+// Source: DeepGEMM README as mirrored on "Weight gradient kernels for dense
+// and MoE models #95", section "V3.2 MQA kernels for the indexer": for query
+// i and every key j in [ks[i], ke[i]),
+//     out[i, j] = sum_h w[i, h] * relu( q[i, h, :] . (kv[j, :] * sf[j]) )
+// with q E4M3 [S, H, D], kv E4M3 [S_kv, D] with one FP32 scale per row,
+// w FP32 [S, H]; positions outside the range are set to -inf when
+// clean_logits is set.  Readings: logits are FP32; ks/ke are clamped to
+// [0, S_kv]; without clean_logits the positions outside the range are left
+// untouched; the kv scales are non-negative (they are quantization scales),
+// so relu(sf * x) = sf * relu(x) and sf is applied once per key after the
+// head sum.
+//
+// Mapping: head_dim D = 128 is exactly one K slab of v_mfma_f32_16x16x128_f8f6f4,
+// so one MFMA gives the dot products of 16 heads of one query with 16 keys.
+//   * A workgroup (4 waves) owns a tile of 128 keys and 32 queries.  The kv
+//     tile (16 KiB) is staged once in LDS with direct global->LDS loads, rows
+//     XOR-swizzled like the GEMM's, and every wave keeps all 8 key fragments
+//     in registers.
+//   * Each wave streams its 8 queries: 4 head fragments of q straight from
+//     global memory (the next query's are loaded while the current one is
+//     computed), 32 MFMAs, and per MFMA output value one max and one FMA with
+//     the head weight.  q is the MFMA's first operand, so a lane holds four
+//     heads of one key and the head sum is four FMAs per lane plus two
+//     cross-lane adds per key.
+//   * Two FP32 VALU operations per (query, head, key) against 256 MFMA flops
+//     put the VALU and the matrix core at about the same peak rate on this
+//     chip, so the kernel is bound by both.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dg.h"
+#include "dg_common.hpp"
+
+namespace {
+
+namespace mqa {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kKeys = 128;     // keys per workgroup tile
+constexpr int kQueries = 32;   // queries per workgroup
+constexpr int kWaves = 4;
+constexpr int kD = 128;        // head dim = one MFMA K slab
+constexpr int kMaxHeads = 64;
+
+struct Params {
+  const uint8_t* q;
+  const uint8_t* kv;
+  const float* sf;
+  const float* w;
+  const int32_t* ks;
+  const int32_t* ke;
+  float* out;
+  int64_t ld_out;
+  int s, s_kv, h;
+  int clean;
+};
+
+__device__ __forceinline__ f32x4 mfma(i32x8 x, i32x8 y) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
+template <int H>
+__global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
+  constexpr int HT = H / 16;  // 16-head fragments per query
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[kKeys * kD];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int key0 = blockIdx.x * kKeys;
+  const int qry0 = blockIdx.y * kQueries;
+
+  // Does any query of this workgroup see a key of this tile?
+  bool any = false;
+  for (int i = qry0 + (tid & 31); i < min(qry0 + kQueries, p.s) && tid < 32; i += 32) {
+    const int lo = min(max(p.ks[i], 0), p.s_kv), hi = min(max(p.ke[i], 0), p.s_kv);
+    any = any || (lo < hi && lo < key0 + kKeys && hi > key0);
+  }
+  any = __syncthreads_or(any);
+
+  i32x8 kvf[kKeys / 16];
+  if (any) {
+    // kv tile -> LDS: 16 direct 1 KiB loads, 4 per wave; row r's 16-byte chunk
+    // c lands at chunk c ^ (r & 7) (the global address is permuted instead).
+    const int ld_row = lane >> 3, ld_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int64_t rows_left = (int64_t)p.s_kv - key0;
+    const uint32_t bytes = rows_left <= 0 ? 0u : (uint32_t)min<int64_t>(rows_left * kD, 0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.kv + (int64_t)key0 * kD), (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kKeys * kD / 1024 / kWaves; ++i) {
+      const int blk = wave * (kKeys * kD / 1024 / kWaves) + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(kv_lds + blk * 1024), 16,
+                                               (uint32_t)((blk * 8 + ld_row) * kD + ld_chunk), 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    __syncthreads();
+    const int sw0 = (q4 ^ (r16 & 7)) << 4, sw1 = ((q4 + 4) ^ (r16 & 7)) << 4;
+#pragma unroll
+    for (int kt = 0; kt < kKeys / 16; ++kt) {
+      const uint8_t* row = kv_lds + (kt * 16 + r16) * kD;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + sw0);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + sw1);
+      kvf[kt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+
+  // this lane stores keys of fragments 2*q4 and 2*q4+1; their scales
+  float sfl[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int key = key0 + (2 * q4 + u) * 16 + r16;
+    sfl[u] = key < p.s_kv ? p.sf[key] : 0.f;
+  }
+
+  // q fragment t of query i: lane holds head 16t + r16, K chunks q4 and q4 + 4
+  auto load_q = [&](int i, i32x8 (&f)[HT]) {
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      const uint8_t* row = p.q + ((int64_t)i * H + t * 16 + r16) * kD;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 16 * q4);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + 64 + 16 * q4);
+      f[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+
+  const int per_wave = kQueries / kWaves;
+  i32x8 qf[HT], qn[HT];
+  int i_first = qry0 + wave;
+  if (any && i_first < p.s) load_q(i_first, qn);
+  for (int n = 0; n < per_wave; ++n) {
+    const int i = qry0 + wave + n * kWaves;
+    if (i >= p.s) break;  // wave-uniform
+    const int lo = min(max(p.ks[i], 0), p.s_kv), hi = min(max(p.ke[i], 0), p.s_kv);
+    const bool live = any && lo < hi && lo < key0 + kKeys && hi > key0;
+#pragma unroll
+    for (int t = 0; t < HT; ++t) qf[t] = qn[t];
+    if (any && n + 1 < per_wave && i + kWaves < p.s) load_q(i + kWaves, qn);
+    float acc[kKeys / 16];
+#pragma unroll
+    for (int kt = 0; kt < kKeys / 16; ++kt) acc[kt] = 0.f;
+    if (live) {
+      // this lane's head weights: heads 16t + 4*q4 + r
+      f32x4 wv[HT];
+#pragma unroll
+      for (int t = 0; t < HT; ++t) wv[t] = *reinterpret_cast<const f32x4*>(p.w + (int64_t)i * H + t * 16 + 4 * q4);
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+#pragma unroll
+        for (int kt = 0; kt < kKeys / 16; ++kt) {
+          const f32x4 pr = mfma(qf[t], kvf[kt]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[kt] = __builtin_fmaf(fmaxf(pr[r], 0.f), wv[t][r], acc[kt]);
+        }
+      }
+      // head sum across the four lane groups (each holds 4 of every 16 heads)
+#pragma unroll
+      for (int kt = 0; kt < kKeys / 16; ++kt) {
+        acc[kt] += __shfl_xor(acc[kt], 16);
+        acc[kt] += __shfl_xor(acc[kt], 32);
+      }
+    }
+    if (!live && !p.clean) continue;
+    float* orow = p.out + (int64_t)i * p.ld_out;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kt = 2 * q4 + u;
+      const int key = key0 + kt * 16 + r16;
+      if (key >= p.s_kv) continue;
+      // acc[kt] with kt known only at run time: select among the unrolled values
+      float v = 0.f;
+#pragma unroll
+      for (int c = 0; c < kKeys / 16; ++c) v = (c == kt) ? acc[c] : v;
+      if (live && key >= lo && key < hi) {
+        orow[key] = v * sfl[u];
+      } else if (p.clean) {
+        orow[key] = -__builtin_inff();
+      }
+    }
+  }
+}
+
+}  // namespace mqa
+
+inline bool aligned_to(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_mqa_logits(const void* q, const void* kv, const float* kv_sf, const float* weights,
+                            const int32_t* ks, const int32_t* ke, float* out, int64_t ld_out, int s, int s_kv,
+                            int num_heads, int head_dim, int clean_logits, hipStream_t stream) {
+  if (s < 0 || s_kv < 0 || num_heads < 0 || head_dim < 0) return DG_ERROR_INVALID_VALUE;
+  if (head_dim != mqa::kD || num_heads % 16 != 0 || num_heads > mqa::kMaxHeads || num_heads == 0)
+    return DG_ERROR_NOT_SUPPORTED;
+  if (s == 0 || s_kv == 0) return DG_SUCCESS;
+  if (q == nullptr || kv == nullptr || kv_sf == nullptr || weights == nullptr || ks == nullptr || ke == nullptr ||
+      out == nullptr)
+    return DG_ERROR_INVALID_VALUE;
+  if (!aligned_to(q, 16) || !aligned_to(kv, 16) || !aligned_to(weights, 16) || !aligned_to(kv_sf, 4) ||
+      !aligned_to(ks, 4) || !aligned_to(ke, 4) || !aligned_to(out, 4))
+    return DG_ERROR_INVALID_VALUE;
+  if (ld_out < s_kv) return DG_ERROR_INVALID_VALUE;
+  if ((int64_t)s_kv * mqa::kD >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
+  const dim3 grid((s_kv + mqa::kKeys - 1) / mqa::kKeys, (s + mqa::kQueries - 1) / mqa::kQueries);
+  if (grid.y > 65535) return DG_ERROR_NOT_SUPPORTED;
+  mqa::Params p{static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kv), kv_sf, weights, ks, ke, out,
+                ld_out, s, s_kv, num_heads, clean_logits != 0};
+  switch (num_heads) {
+    case 16: hipLaunchKernelGGL(mqa::logits_kernel<16>, grid, dim3(mqa::kWaves * 64), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(mqa::logits_kernel<32>, grid, dim3(mqa::kWaves * 64), 0, stream, p); break;
+    case 48: hipLaunchKernelGGL(mqa::logits_kernel<48>, grid, dim3(mqa::kWaves * 64), 0, stream, p); break;
+    default: hipLaunchKernelGGL(mqa::logits_kernel<64>, grid, dim3(mqa::kWaves * 64), 0, stream, p); break;
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DG_SUCCESS : dg::record_hip_error(e);
+}
+
+}  // extern "C"

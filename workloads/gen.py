@@ -318,7 +318,7 @@ DENSE_SWEEP = [(m, n, k) for m in DENSE_SWEEP_M for (n, k) in DENSE_SWEEP_NK]
 
 WORKLOAD_NAMES = ("dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc",
                   "dense_sweep_ue8m0", "contiguous_moe_ue8m0", "masked_decode_ue8m0", "k_grouped_wgrad",
-                  "quant_moe")
+                  "quant_moe", "mqa_logits")
 
 
 def workload(name: str):
@@ -374,6 +374,10 @@ def workload(name: str):
                 dict(label="per-block cast BF16 [32768, 7168]", kind="quant_block", m=32768, k=7168,
                      gen=lambda: dict(kind="quant_block", m=32768, k=7168, dtype="bf16",
                                       x=gen_quant_input(32768, 7168, seed=7)))]
+    if name == "mqa_logits":
+        # indexer prefill: 4096 new tokens over a 4096-token cached prefix, 64 heads of dim 128
+        return [dict(label="mqa logits S=4096 S_kv=8192 H=64 D=128 causal", kind="mqa", s=4096, s_kv=8192,
+                     gen=lambda: gen_mqa(4096, 8192, 64, 128, seed=8, ranges="causal"))]
     if name == "dense_long_k_acc":
         return [dict(label="dense+C M=8192 N=8192 K=16384 fp32", kind="dense", m=8192, n=8192, k=16384,
                      gen=lambda: gen_dense(8192, 8192, 16384, seed=4, with_c=True, out_dtype="fp32"))]
