@@ -262,8 +262,14 @@ def time_launches(case: Case, iters: int, flush=None):
     return times[len(times) // 2]
 
 
-def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
-    """Time the FP64 oracle on a bounded sample (first rows x first columns of every case)."""
+def cpu_baseline(inputs, budget_rows=4096, budget_cols=24576, quant_rows=8192):
+    """Time the oracle on a bounded sample of the step's inputs.
+
+    GEMMs: the first ``budget_rows`` output rows (masked: the first two groups;
+    K-grouped: every group) x the first ``budget_cols`` columns of every case,
+    which is the whole step for the dense sweep; MQA: every query; casts: the
+    first ``quant_rows`` rows.  Returns TFLOPS (or GB/s for the casts) of the
+    oracle on the host's cores."""
     import numpy as np
     import oracle
     try:
@@ -272,59 +278,56 @@ def cpu_baseline(inputs, budget_rows=2048, budget_cols=16384):
     except Exception:  # pragma: no cover
         threads = 1
     total_flops, total_bytes, total_s = 0.0, 0.0, 0.0
+    parts = []
     for x in inputs:
-        k = x["k"]
+        kind = x["kind"]
         t0 = time.perf_counter()
-        if x["kind"] not in ("quant_token", "quant_block", "mqa"):
-            n = x["n"]
-            cols = np.arange(min(n, budget_cols))
-        if x["kind"] == "mqa":
-            rows = np.arange(0, x["s"], max(1, x["s"] // 64))
-            oracle.ref_mqa_logits(x["q"], x["kv"], x["sf"], x["w"], x["ks"], x["ke"], True, rows=rows)
-            total_s += time.perf_counter() - t0
-            lo = np.clip(x["ks"][rows], 0, x["s_kv"])
-            hi = np.clip(x["ke"][rows], 0, x["s_kv"])
+        if kind == "mqa":
+            oracle.ref_mqa_logits(x["q"], x["kv"], x["sf"], x["w"], x["ks"], x["ke"], True)
+            lo = np.clip(x["ks"], 0, x["s_kv"])
+            hi = np.clip(x["ke"], 0, x["s_kv"])
             total_flops += 2.0 * x["h"] * x["d"] * float(np.maximum(hi - lo, 0).sum())
-            continue
-        if x["kind"] in ("quant_token", "quant_block"):
-            nrows = min(x["m"], budget_rows)
-            xs = x["x"][:nrows]
-            (oracle.quant_per_token if x["kind"] == "quant_token" else oracle.quant_per_block)(xs)
-            total_s += time.perf_counter() - t0
-            total_bytes += nrows * k * (2 if x["dtype"] == "bf16" else 4) + nrows * k
-            continue
-        ue = x.get("scale_fmt") == "ue8m0"
-        kk = k
-        if x["kind"] == "k_grouped":
-            rows = np.arange(min(x["m"], budget_rows // 4))
-            oracle.ref_k_grouped(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], x.get("c"), rows=rows, cols=cols)
-            nrows = len(rows)
-        elif x["kind"] == "dense":
-            rows = np.arange(min(x["m"], budget_rows))
-            ref = oracle.ref_dense_ue8m0 if ue else oracle.ref_dense
-            ref(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"), rows=rows, cols=cols)
-            nrows = len(rows)
-        elif x["kind"] == "contiguous":
-            valid = np.nonzero(x["m_indices"] >= 0)[0][:budget_rows]
-            ref = oracle.ref_contiguous_ue8m0 if ue else oracle.ref_contiguous
-            ref(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"], rows=valid, cols=cols)
-            nrows = len(valid)
+            parts.append(f"all {x['s']} queries")
+        elif kind in ("quant_token", "quant_block"):
+            nrows = min(x["m"], quant_rows)
+            (oracle.quant_per_token if kind == "quant_token" else oracle.quant_per_block)(x["x"][:nrows])
+            total_bytes += nrows * x["k"] * (2 if x["dtype"] == "bf16" else 4) + nrows * x["k"]
+            parts.append(f"{nrows} of {x['m']} rows")
         else:
-            groups = np.arange(min(x["num_groups"], 2))
-            ref = oracle.ref_masked_ue8m0 if ue else oracle.ref_masked
-            ref(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
-            nrows = int(np.clip(x["masked_m"][groups], 0, x["m_max"]).sum())
+            n, k = x["n"], x["k"]
+            cols = np.arange(min(n, budget_cols))
+            ue = x.get("scale_fmt") == "ue8m0"
+            if kind == "k_grouped":
+                rows = np.arange(min(x["m"], budget_rows))
+                oracle.ref_k_grouped(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], x.get("c"), rows=rows, cols=cols)
+                nrows = len(rows)
+            elif kind == "dense":
+                rows = np.arange(min(x["m"], budget_rows))
+                ref = oracle.ref_dense_ue8m0 if ue else oracle.ref_dense
+                ref(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"), rows=rows, cols=cols)
+                nrows = len(rows)
+            elif kind == "contiguous":
+                valid = np.nonzero(x["m_indices"] >= 0)[0][:budget_rows]
+                ref = oracle.ref_contiguous_ue8m0 if ue else oracle.ref_contiguous
+                ref(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"], rows=valid, cols=cols)
+                nrows = len(valid)
+            else:
+                groups = np.arange(min(x["num_groups"], 2))
+                ref = oracle.ref_masked_ue8m0 if ue else oracle.ref_masked
+                ref(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
+                nrows = int(np.clip(x["masked_m"][groups], 0, x["m_max"]).sum())
+            total_flops += 2.0 * nrows * len(cols) * k
+            parts.append(f"{nrows} rows x {len(cols)} cols")
         total_s += time.perf_counter() - t0
-        total_flops += 2.0 * nrows * len(cols) * kk
+    host = len(os.sched_getaffinity(0))
     if total_flops == 0:
         return dict(value=total_bytes / total_s / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                    sample=f"first {budget_rows} rows of every case, numpy FP32 cast, "
-                           f"{total_bytes / 1e6:.1f} MB in {total_s:.1f} s",
-                    host_cpus=len(os.sched_getaffinity(0)))
+                    sample=f"numpy FP32 cast of {'; '.join(parts)}: {total_bytes / 1e6:.1f} MB in {total_s:.1f} s",
+                    host_cpus=host)
     return dict(value=total_flops / total_s / 1e12, unit="TFLOPS", cores=int(threads), kind="oracle",
-                sample=f"first {budget_rows} valid rows x first {budget_cols} columns of every case "
-                       f"(masked: first 2 groups), FP64 numpy, {total_flops / 1e9:.1f} GFLOP in {total_s:.1f} s",
-                host_cpus=len(os.sched_getaffinity(0)))
+                sample=f"FP64 numpy oracle over {'; '.join(parts)} of the step's cases: "
+                       f"{total_flops / 1e9:.1f} GFLOP in {total_s:.1f} s",
+                host_cpus=host)
 
 
 def main():
