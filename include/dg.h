@@ -4,8 +4,10 @@
  *
  * Computes D = C + A @ B.T in NT layout (A row-major [M,K], B row-major
  * [N,K], i.e. both K-contiguous) where A and B hold OCP E4M3 (E4M3FN) byte
- * codes, A carries one FP32 scale per (row, 128-wide K block) and B one FP32
- * scale per 128x128 block.  Sources, by page title and section:
+ * codes, A carries one FP32 (or UE8M0) scale per (row, 128-wide K block) and
+ * B one per 128x128 block; plus the K-grouped / weight-gradient GEMMs, the FP8
+ * cast that produces the operands, and the MQA logits of the indexer.
+ * Sources, by page title and section:
  *
  *   [README]  DeepGEMM README as mirrored on the page "Weight gradient
  *             kernels for dense and MoE models #95" (English); the same text
@@ -38,12 +40,13 @@
  *     never an error: out-of-range values are clamped or skipped so that all
  *     memory accesses stay in bounds.
  *
- * Workspace: some shapes (small M, few tiles) split K across workgroups.
- * Their FP32 partial sums go to a per-device workspace that the library
- * allocates the first time a shape needs it (hipMalloc outside the caller's
- * stream order) and keeps until process exit.  A call that needs a larger
- * workspace than the current one grows it; calls under graph capture must
- * therefore be preceded by one uncaptured call of the same shape.
+ * Workspace: skinny dense GEMMs (M <= 128, K >= 1024) split K across
+ * workgroups.  Their FP32 partial sums go to a workspace the library keeps
+ * per (device, stream): allocated with hipMalloc the first time a shape on
+ * that stream needs it, grown (after synchronising that stream) when a larger
+ * shape needs more, kept until process exit.  Calls under graph capture must
+ * therefore be preceded by one uncaptured call of the same shape on the
+ * capture stream; a captured graph uses that stream's workspace.
  */
 #ifndef DG_H
 #define DG_H
