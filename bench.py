@@ -60,7 +60,7 @@ def lookup_traffic(case_label: str):
     return None if ent is None else ent.get("traffic_bytes")
 
 
-def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str):
+def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, kernel: str = "gemm_kernel"):
     """Summarise rocprofv3 output (trace/, fetch/, write/ under prof_dir) into a short text file and
     record the calibrated HBM traffic of the GEMM kernel in profiles/traffic.json."""
     import csv
@@ -83,8 +83,8 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str):
         vals = [v for k, vs in per.items() if pred(k) for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    is_gemm = lambda k: "gemm_kernel" in k
-    is_copy = lambda k: "copy" in k.lower() and "gemm" not in k
+    is_gemm = lambda k: kernel in k
+    is_copy = lambda k: "copy" in k.lower() and kernel not in k
     cal_bytes = COPY_CAL_MB * (1 << 20)
     f_gemm = mean_of(counters["FETCH_SIZE"], is_gemm)
     w_gemm = mean_of(counters["WRITE_SIZE"], is_gemm)
@@ -104,7 +104,7 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str):
         traffic = f_gemm * 1024 / kf + w_gemm * 1024 / kw
         lines += [f"- copy calibration ({COPY_CAL_MB} MiB device copy): FETCH_SIZE {f_copy:.0f} KiB "
                   f"(factor {kf:.3f}), WRITE_SIZE {w_copy:.0f} KiB (factor {kw:.3f})",
-                  f"- GEMM kernel: FETCH_SIZE {f_gemm:.0f} KiB, WRITE_SIZE {w_gemm:.0f} KiB per dispatch",
+                  f"- `{kernel}`: FETCH_SIZE {f_gemm:.0f} KiB, WRITE_SIZE {w_gemm:.0f} KiB per dispatch",
                   f"- calibrated HBM traffic per launch: {traffic / 1e6:.1f} MB"]
         rec = {}
         try:
@@ -345,10 +345,11 @@ def main():
     ap.add_argument("--profile-summary", nargs=3, metavar=("PROF_DIR", "OUT_MD", "CASE_LABEL"),
                     help="summarise rocprofv3 output collected for CASE_LABEL and exit (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command line recorded in the profile summary")
+    ap.add_argument("--profile-kernel", default="gemm_kernel", help="name substring of the profiled kernel")
     args = ap.parse_args()
 
     if args.profile_summary:
-        profile_summary(*args.profile_summary, command=args.profile_command)
+        profile_summary(*args.profile_summary, command=args.profile_command, kernel=args.profile_kernel)
         return
 
     if args.gpus != 1:
