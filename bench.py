@@ -76,20 +76,25 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
         per = {}
         for r in rows(sub, "*counter_collection.csv"):
             if r["Counter_Name"] == name:
-                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                per.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
         counters[name] = per
 
     def mean_of(per, pred):
-        vals = [v for k, vs in per.items() if pred(k) for v in vs]
+        vals = [v for k, vs in per.items() if pred(k) for _, v in vs]
         return sum(vals) / len(vals) if vals else None
+
+    def first_of(per, pred):
+        # the calibration copy is the process's first copy dispatch (input uploads come later)
+        vals = sorted((d, v) for k, vs in per.items() if pred(k) for d, v in vs)
+        return vals[0][1] if vals else None
 
     is_gemm = lambda k: kernel in k
     is_copy = lambda k: "copy" in k.lower() and kernel not in k
     cal_bytes = COPY_CAL_MB * (1 << 20)
     f_gemm = mean_of(counters["FETCH_SIZE"], is_gemm)
     w_gemm = mean_of(counters["WRITE_SIZE"], is_gemm)
-    f_copy = mean_of(counters["FETCH_SIZE"], is_copy)
-    w_copy = mean_of(counters["WRITE_SIZE"], is_copy)
+    f_copy = first_of(counters["FETCH_SIZE"], is_copy)
+    w_copy = first_of(counters["WRITE_SIZE"], is_copy)
     lines = [f"# rocprofv3 summary: {case_label}", "", "Command (run from the repository root):", "", "```",
              command, "```", "", "## Kernel trace (--kernel-trace --stats)", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
