@@ -21,10 +21,11 @@
 //     in registers.
 //   * Each wave streams its 8 queries: 4 head fragments of q straight from
 //     global memory (the next query's are loaded while the current one is
-//     computed), 32 MFMAs, and per MFMA output value one max and one FMA with
-//     the head weight.  q is the MFMA's first operand, so a lane holds four
-//     heads of one key and the head sum is four FMAs per lane plus two
-//     cross-lane adds per key.
+//     computed), 32 MFMAs, and per MFMA output value one integer max (the
+//     ReLU) and one FMA with the head weight, issued three MFMAs behind.
+//     q is the MFMA's first operand, so a lane holds four heads of one key
+//     and the head sum is four FMAs per lane plus two lane swaps
+//     (v_permlane32_swap, v_permlane16_swap) and adds per key.
 //   * Two FP32 VALU operations per (query, head, key) against 256 MFMA flops
 //     put the VALU and the matrix core at about the same peak rate on this
 //     chip, so the kernel is bound by both.
@@ -62,6 +63,43 @@ struct Params {
   int s, s_kv, h;
   int clean;
 };
+
+// Head sum of the 8 per-key partial sums of a lane across the four lane
+// groups (each group holds 4 of every 16 heads), scattered so that lane group
+// g ends with the sums of keys 2g and 2g+1 of the tile -- the two it stores.
+// v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) by 32-lane
+// halves and v_permlane16_swap the same by 16-lane rows (checked on gfx950),
+// so one swap and one add fold two values at once; six swaps and six adds in
+// all, on the VALU (no trip through the LDS unit as __shfl_xor takes).
+__device__ __forceinline__ void head_sum_scatter(const float (&acc)[8], float (&out)[2]) {
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k]), __float_as_uint(acc[k + 4]), false, false);
+    r[k] = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // halves: key k (lanes 0-31), key k+4 (32-63)
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(r[k]), __float_as_uint(r[k + 2]), false, false);
+    out[k] = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows: keys k, k+2, k+4, k+6
+  }
+}
+
+// max(x, 0) for a float as one integer max on its bits: negative values
+// (sign bit set) become +0, everything else is kept.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Wave-uniform load through the scalar cache: a uniform address in the
+// constant address space makes the compiler emit s_load (counted by lgkmcnt
+// only; a flat load would also occupy the vector-load counter and make the
+// value a per-lane one).  The ranges are read-only during the kernel.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *reinterpret_cast<const_i32_ptr>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 __device__ __forceinline__ f32x4 mfma(i32x8 x, i32x8 y) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -122,70 +160,79 @@ __global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
     sfl[u] = key < p.s_kv ? p.sf[key] : 0.f;
   }
 
-  // q fragment t of query i: lane holds head 16t + r16, K chunks q4 and q4 + 4
-  auto load_q = [&](int i, i32x8 (&f)[HT]) {
+  // Operands of query i: q fragment t (lane holds head 16t + r16, K chunks q4
+  // and q4 + 4) and the lane's head weights (heads 16t + 4*q4 + r).  Both are
+  // loaded one query ahead; loading the weights just before use would make
+  // their wait (vector loads complete in order) also wait for the prefetch.
+  auto load_q = [&](int i, i32x8 (&f)[HT], f32x4 (&wt)[HT]) {
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
       const uint8_t* row = p.q + ((int64_t)i * H + t * 16 + r16) * kD;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 16 * q4);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(row + 64 + 16 * q4);
       f[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      wt[t] = *reinterpret_cast<const f32x4*>(p.w + (int64_t)i * H + t * 16 + 4 * q4);
     }
   };
 
   const int per_wave = kQueries / kWaves;
-  i32x8 qf[HT], qn[HT];
-  int i_first = qry0 + wave;
-  if (any && i_first < p.s) load_q(i_first, qn);
-  for (int n = 0; n < per_wave; ++n) {
+  static_assert(kQueries % (2 * kWaves) == 0, "queries come in pairs per wave");
+  i32x8 qa[HT], qb[HT];
+  f32x4 wa[HT], wb[HT];
+
+  // One query: uses (qc, wc), prefetches query i + kWaves into (qn, wn).  The
+  // prefetch is unconditional (the index is clamped to a valid query): with a
+  // path that skips it, the loop's join would have to wait for every load in
+  // flight, the prefetch included.
+  auto one_query = [&](int n, i32x8 (&qc)[HT], f32x4 (&wc)[HT], i32x8 (&qn)[HT], f32x4 (&wn)[HT])
+                       __attribute__((always_inline)) {
     const int i = qry0 + wave + n * kWaves;
-    if (i >= p.s) break;  // wave-uniform
-    const int lo = min(max(p.ks[i], 0), p.s_kv), hi = min(max(p.ke[i], 0), p.s_kv);
+    if (i >= p.s) return;  // wave-uniform
+    const int lo = min(max(load_uniform_i32(p.ks + i), 0), p.s_kv);
+    const int hi = min(max(load_uniform_i32(p.ke + i), 0), p.s_kv);
     const bool live = any && lo < hi && lo < key0 + kKeys && hi > key0;
-#pragma unroll
-    for (int t = 0; t < HT; ++t) qf[t] = qn[t];
-    if (any && n + 1 < per_wave && i + kWaves < p.s) load_q(i + kWaves, qn);
-    float acc[kKeys / 16];
-#pragma unroll
-    for (int kt = 0; kt < kKeys / 16; ++kt) acc[kt] = 0.f;
+    load_q(min(i + kWaves, p.s - 1), qn, wn);
+    float sums[2] = {0.f, 0.f};
     if (live) {
-      // this lane's head weights: heads 16t + 4*q4 + r
-      f32x4 wv[HT];
+      float acc[kKeys / 16];
 #pragma unroll
-      for (int t = 0; t < HT; ++t) wv[t] = *reinterpret_cast<const f32x4*>(p.w + (int64_t)i * H + t * 16 + 4 * q4);
+      for (int kt = 0; kt < kKeys / 16; ++kt) acc[kt] = 0.f;
+      // Flat sequence of the HT * 8 MFMAs (head fragment t = s / 8, key
+      // fragment kt = s % 8); the ReLU and weight FMAs of MFMA s - (RING - 1)
+      // are issued after MFMA s, so they run under the matrix core.
+      constexpr int T = HT * (kKeys / 16);
+      constexpr int RING = 4;
+      f32x4 part[RING];
 #pragma unroll
-      for (int t = 0; t < HT; ++t) {
+      for (int st = 0; st < T + RING - 1; ++st) {
+        if (st < T) part[st % RING] = mfma(qc[st / (kKeys / 16)], kvf[st % (kKeys / 16)]);
+        const int v = st - (RING - 1);
+        if (v >= 0) {
+          const int t = v / (kKeys / 16), kt = v % (kKeys / 16);
 #pragma unroll
-        for (int kt = 0; kt < kKeys / 16; ++kt) {
-          const f32x4 pr = mfma(qf[t], kvf[kt]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[kt] = __builtin_fmaf(fmaxf(pr[r], 0.f), wv[t][r], acc[kt]);
+          for (int r = 0; r < 4; ++r) acc[kt] = __builtin_fmaf(relu(part[v % RING][r]), wc[t][r], acc[kt]);
         }
       }
-      // head sum across the four lane groups (each holds 4 of every 16 heads)
-#pragma unroll
-      for (int kt = 0; kt < kKeys / 16; ++kt) {
-        acc[kt] += __shfl_xor(acc[kt], 16);
-        acc[kt] += __shfl_xor(acc[kt], 32);
-      }
+      head_sum_scatter(acc, sums);
     }
-    if (!live && !p.clean) continue;
+    if (!live && !p.clean) return;
     float* orow = p.out + (int64_t)i * p.ld_out;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int kt = 2 * q4 + u;
-      const int key = key0 + kt * 16 + r16;
+      const int key = key0 + (2 * q4 + u) * 16 + r16;
       if (key >= p.s_kv) continue;
-      // acc[kt] with kt known only at run time: select among the unrolled values
-      float v = 0.f;
-#pragma unroll
-      for (int c = 0; c < kKeys / 16; ++c) v = (c == kt) ? acc[c] : v;
       if (live && key >= lo && key < hi) {
-        orow[key] = v * sfl[u];
+        orow[key] = sums[u] * sfl[u];
       } else if (p.clean) {
         orow[key] = -__builtin_inff();
       }
     }
+  };
+
+  load_q(min(qry0 + wave, p.s - 1), qa, wa);
+  for (int n = 0; n < per_wave; n += 2) {
+    one_query(n, qa, wa, qb, wb);
+    one_query(n + 1, qb, wb, qa, wa);
   }
 }
 
@@ -227,3 +274,4 @@ dg_status dg_fp8_mqa_logits(const void* q, const void* kv, const float* kv_sf, c
 }
 
 }  // extern "C"
+
