@@ -33,16 +33,29 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (no sparsity)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "moe_grouped_gemm_tiles_amd", "csrc")
-KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+# Sources whose change invalidates a traffic record, per kernel family.
+KERNEL_SOURCES = {
+    "gemm": ["dg_kernels.hpp", "dg_api.hip", "dg_common.hpp"],
+    "quant": ["dg_quant.hip", "dg_common.hpp"],
+    "mqa": ["dg_mqa.hip", "dg_common.hpp"],
+}
+
+
+def kernel_family(case_label: str) -> str:
+    if case_label.startswith("mqa"):
+        return "mqa"
+    if "cast" in case_label:
+        return "quant"
+    return "gemm"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_CAL_MB = 256  # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -54,10 +67,10 @@ def lookup_traffic(case_label: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
-        return None  # kernel changed since the counters were taken
     ent = rec.get("cases", {}).get(case_label)
-    return None if ent is None else ent.get("traffic_bytes")
+    if ent is None or ent.get("source_hash") != kernel_source_hash(kernel_family(case_label)):
+        return None  # no record, or the kernel changed since the counters were taken
+    return ent.get("traffic_bytes")
 
 
 def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, kernel: str = "gemm_kernel"):
@@ -116,10 +129,11 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
             rec = json.load(open(TRAFFIC_FILE))
         except (OSError, ValueError):
             pass
-        if rec.get("source_hash") != kernel_source_hash():
-            rec = {"source_hash": kernel_source_hash(), "cases": {}}
+        rec.setdefault("cases", {})
+        rec.pop("source_hash", None)
         rec["cases"][case_label] = {"traffic_bytes": traffic, "fetch_kib": f_gemm, "write_kib": w_gemm,
-                                    "fetch_factor": kf, "write_factor": kw}
+                                    "fetch_factor": kf, "write_factor": kw,
+                                    "source_hash": kernel_source_hash(kernel_family(case_label))}
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
