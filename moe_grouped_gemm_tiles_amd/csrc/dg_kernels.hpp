@@ -90,30 +90,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until at most `pending` slabs of loads (of `per` instructions each) are
-// still outstanding; `pending` is a runtime value in [0, MAXP].
-template <int MAXP, int PER>
-__device__ __forceinline__ void wait_slabs_pending(int pending) {
-  if constexpr (MAXP <= 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (pending >= MAXP) {
-      wait_vmcnt<MAXP * PER>();
-    } else {
-      wait_slabs_pending<MAXP - 1, PER>(pending);
-    }
-  }
-}
-
-// Uniform (scalar-cache) load of one float: the address is made wave-uniform
-// so the compiler emits s_load_dword, which is counted by lgkmcnt, not vmcnt.
-__device__ __forceinline__ float load_uniform_f32(const float* ptr) {
-  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return *reinterpret_cast<const float*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
 // Workgroup barrier of the staging ring.  The caller has already waited for
 // its own loads of the slab about to be read (vmcnt); this adds the wait for
 // the wave's own LDS reads (a stage is overwritten only after every wave has
@@ -157,12 +133,14 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128_e8m0(i32x8 x, i32x8 y, f32x4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
 }
 
-// FP32 -> BF16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two FP32 -> BF16 conversions with v_cvt_pk_bf16_f32: round to nearest
+// even, NaN stays a quiet NaN (checked bit-for-bit against the integer
+// rounding u + 0x7fff + ((u >> 16) & 1) on all 2^32 inputs).
+__device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Two 16-byte reads of a swizzled 128-byte LDS row: the lane's 32 K-bytes of
@@ -217,13 +195,13 @@ __device__ __forceinline__ void store_out(const Params& p, int64_t crow, int gn,
   if (BF16_OUT) {
     uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
     if (full) {
-      const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-      const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+      const uint32_t lo = bf16x2_rne_bits(v[0], v[1]);
+      const uint32_t hi = bf16x2_rne_bits(v[2], v[3]);
       *reinterpret_cast<uint2*>(D) = make_uint2(lo, hi);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (gn + r < p.n) D[r] = (uint16_t)bf16_rne_bits(v[r]);
+        if (gn + r < p.n) D[r] = (uint16_t)bf16x2_rne_bits(v[r], 0.f);
     }
   } else {
     float* D = reinterpret_cast<float*>(p.d) + drow + gn;
@@ -246,22 +224,30 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, SFA_BYTES = BM * 4;
-  constexpr int STAGE = A_BYTES + B_BYTES + SFA_BYTES;
+  constexpr int SFB_SLOTS = (BN + 127) / 128;  // B-scale words per slab: one per 128-column block of the tile
+  constexpr int SFB_OFF = A_BYTES + B_BYTES + SFA_BYTES;
+  // stages start on 256-byte boundaries, so every stage has the same bank phase
+  constexpr int STAGE = (SFB_OFF + 4 * SFB_SLOTS + 255) / 256 * 256;
   constexpr int A_LOADS = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per slab
   constexpr int B_LOADS = B_BYTES / 1024 / NW;
+  constexpr int LOADS = A_LOADS + B_LOADS;
   constexpr int SFA_LANES = BM / 4;  // lanes of wave 0 that stage the slab's row scales (16 B each)
+  // Slab schedule (see the K loop): the last HOLD fragment rows of a slab are
+  // multiplied after the slab's barrier; partial t is promoted after MFMA t + LAG.
+  constexpr int HOLD = 2, FIRST = FM - HOLD;
+  constexpr int T = FM * FN, T1 = FIRST * FN, P2 = HOLD * FN;
+  constexpr int RING = 4, LAG = 3;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
   static_assert(128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
-  static_assert(FN >= 2, "the promotion ring lags at most one 16-row fragment behind");
+  static_assert(FIRST >= HOLD && FN >= 2, "two-part slab schedule");
+  static_assert(T % RING == 0 && LAG < RING && LAG <= P2, "promotion ring");
   static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "loads must split evenly");
   static_assert(SFA_LANES >= 1 && SFA_LANES <= 64 && SFA_LANES * 16 == SFA_BYTES, "sfa staging");
+  static_assert(NW >= 2, "the A and B scale loads ride on different waves");
   static_assert(MODE != MODE_CONTIG || BM == 128 || BM == 256, "contiguous tiles cover one or two 128-row blocks");
   static_assert(!SPLIT || MODE == MODE_DENSE, "split-K is for dense GEMMs");
   static_assert(MODE != MODE_KGROUP || !BF16_OUT, "K-grouped outputs are FP32");
   static_assert(STAGES >= 2, "at least double buffering");
-  // Per-wave load instructions per slab (wave 0 issues one more, for the row
-  // scales; using the smaller count makes wave 0 wait slightly longer).
-  constexpr int LOADS_PER_SLAB = A_LOADS + B_LOADS;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
 
@@ -353,23 +339,60 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       for (int i = 0; i < B_LOADS; ++i)
         b_off[i] = (uint32_t)(((wave * B_LOADS + i) * 8 + ld_row) * p.ldb) + ld_chunk;
 
-      // scale block of this wave's columns (clamped: columns past N are never stored)
-      const int sfb_blk = min((n0 + wn * TN) >> 7, NBLK - 1);
-      const float* SFB_w = SFB + (int64_t)sfb_blk * (E8M0 ? KQ : KB);
+      // B-scale words staged with each slab: slot u holds block min(n0/128 + u, NBLK-1)
+      // (clamped: columns past N are never stored)
+      const int sfb_row = E8M0 ? KQ : KB;
+      const uint32_t sfb_off = (uint32_t)(min((n0 >> 7) + lane, NBLK - 1) * sfb_row) * 4;
+      const uint32_t sfb_bytes = (uint32_t)(NBLK * sfb_row) * 4;
 
-      auto issue_slab = [&](int kb, int stage) {
+      // Descriptors of slab kb; a slab past the tile's K range gets empty
+      // descriptors, so its loads (issued anyway, which keeps the wait counts
+      // fixed) fetch nothing and write zeros.
+      struct SlabRsrc {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        int kb;
+        bool live;
+      };
+      auto slab_rsrc = [&](int kb, bool live) {
+        SlabRsrc r;
+        r.ra = make_rsrc(A + kb * 128, live ? clamp_bytes(a_rows * p.lda - kb * 128) : 0u);
+        r.rb = make_rsrc(B + kb * 128, live ? clamp_bytes(b_rows * p.ldb - kb * 128) : 0u);
+        r.kb = kb;
+        r.live = live;
+        return r;
+      };
+      // Load idx of the wave's LOADS direct loads of a slab into `stage`
+      // (idx < A_LOADS: A rows, else B rows); idx 0 also stages the scales
+      // (A row scales on wave 0, B block scales on the last wave).
+      auto issue_load = [&](const SlabRsrc& r, int stage, int idx) {
         uint8_t* base = lds + stage * STAGE;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + kb * 128, clamp_bytes(a_rows * p.lda - kb * 128));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + kb * 128, clamp_bytes(b_rows * p.ldb - kb * 128));
+        if (idx < A_LOADS) {
+          load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
+        } else {
+          load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
+        }
+        if (idx == 0) {
+          const int q = E8M0 ? (r.kb >> 2) : r.kb;  // scale row (A) / column (B) of the slab
+          if (wave == 0 && lane < SFA_LANES)
+            load_to_lds16(make_rsrc(SFA + (int64_t)q * p.ld_sfa, r.live ? clamp_bytes(a_rows * 4) : 0u),
+                          base + A_BYTES + B_BYTES, lane * 16);
+          if (wave == NW - 1 && lane < SFB_SLOTS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(SFB + q, r.live ? clamp_bytes((int64_t)sfb_bytes - 4 * q) : 0u),
+                                                     (lds_ptr_t)(base + SFB_OFF), 4, sfb_off, 0, 0, 0);
+        }
+      };
+      auto issue_slab = [&](int kb, int stage, bool live) {
+        const SlabRsrc r = slab_rsrc(kb, live);
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) load_to_lds16(ra, base + (wave * A_LOADS + i) * 1024, a_off[i]);
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-          load_to_lds16(rb, base + A_BYTES + (wave * B_LOADS + i) * 1024, b_off[i]);
-        if (wave == 0 && lane < SFA_LANES) {
-          const int sf_row = E8M0 ? (kb >> 2) : kb;
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(SFA + (int64_t)sf_row * p.ld_sfa, clamp_bytes(a_rows * 4));
-          load_to_lds16(rs, base + A_BYTES + B_BYTES, lane * 16);
+        for (int idx = 0; idx < LOADS; ++idx) issue_load(r, stage, idx);
+      };
+      // Wait until this wave's loads of the slab STAGES-2 slabs before the
+      // newest issued one have landed (waves 0 and NW-1 issue one more load per slab).
+      auto wait_slab = [&]() {
+        if (wave == 0 || wave == NW - 1) {
+          wait_vmcnt<(STAGES - 2) * (LOADS + 1)>();
+        } else {
+          wait_vmcnt<(STAGES - 2) * LOADS>();
         }
       };
 
@@ -379,87 +402,145 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      // prologue: STAGES-1 slabs in flight
+      // K loop.  One workgroup barrier per slab, placed inside the slab's
+      // MFMAs: part 1 multiplies fragment rows 0 .. FIRST-1 (row-major,
+      // A fragments streamed from LDS) and reads the slab's last HOLD A
+      // fragments into registers; at the barrier every wave has finished
+      // reading slab `it` (its stage takes slab it + STAGES) and slab it + 1 has
+      // landed; part 2 multiplies rows FIRST .. FM-1 (column-major) from
+      // registers only, issuing one direct load of slab it + STAGES per MFMA
+      // and reading slab it + 1's B fragments, first A fragment and scales as
+      // the columns free up.  No LDS latency and no burst of loads sits at the
+      // barrier.  Each slab's FP32 promotion trails its MFMAs by LAG and
+      // carries across the slab boundary.
+      // fragment row / column of the slab's MFMA t
+      auto row_of = [](int t) { return t < T1 ? t / FN : FIRST + (t - T1) % HOLD; };
+      auto col_of = [](int t) { return t < T1 ? t % FN : (t - T1) / HOLD; };
+      if (nkb > 0) {
 #pragma unroll
-      for (int i = 0; i < STAGES - 1; ++i)
-        if (i < nkb) issue_slab(kb_begin + i, i);
-      // scale of this wave's B block for slab kb (UE8M0: the word holding it)
-      auto sfb_of = [&](int kb) { return load_uniform_f32(SFB_w + (E8M0 ? (kb >> 2) : kb)); };
-      float sb_next = nkb > 0 ? sfb_of(kb_begin) : 0.f;
+        for (int i = 0; i < STAGES - 1; ++i) issue_slab(kb_begin + i, i, i < nkb);
+        wait_slab();
+        stage_barrier();
+        issue_slab(kb_begin + STAGES - 1, STAGES - 1, STAGES - 1 < nkb);
 
-      for (int it = 0; it < nkb; ++it) {
-        const int cur = it % STAGES;
-        const float sb = sb_next;
-        // slabs issued after slab `it` that may stay in flight
-        wait_slabs_pending<STAGES - 2, LOADS_PER_SLAB>(min(STAGES - 2, nkb - 1 - it));
-        stage_barrier();  // slab `it` has landed for every wave; stage (it-1) % STAGES is free
-        if (it + STAGES - 1 < nkb) issue_slab(kb_begin + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-        if (it + 1 < nkb) sb_next = sfb_of(kb_begin + it + 1);
-        if (wave_live && E8M0) {
-          // UE8M0: scales go into the MFMA, which accumulates across slabs
-          const int sh = 8 * ((kb_begin + it) & 3);
-          const int sbx = (int)(__float_as_uint(sb) >> sh);
-          const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
-          const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
-          const uint32_t* Sw = reinterpret_cast<const uint32_t*>(lds + cur * STAGE + A_BYTES + B_BYTES) + wm * TM + r16;
-          i32x8 fb[FN];
+        const uint8_t* As0 = lds + (wm * TM + r16) * 128;
+        const uint8_t* Bs0 = lds + A_BYTES + (wn * TN + r16) * 128;
+        const uint8_t* Ss0 = lds + A_BYTES + B_BYTES + (wm * TM + r16) * 4;
+        const uint8_t* Sb0 = lds + SFB_OFF + ((wn * TN) >> 7) * 4;
+
+        // slab 0's fragments, read in the order part 2 reads the next slab's,
+        // so that the waits at the loop head agree on both paths into it
+        i32x8 fb[FN], fh[HOLD];
+        fb[0] = read_frag(Bs0, sw0, sw1);
+        i32x8 fa = read_frag(As0, sw0, sw1), fa_next = fa;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) fb[j] = read_frag(Bs + j * 16 * 128, sw0, sw1);
-          i32x8 fa = read_frag(As, sw0, sw1);
-          int sa = (int)(Sw[0] >> sh);
+        for (int j = 1; j < FN; ++j) {
+          fb[j] = read_frag(Bs0 + j * 16 * 128, sw0, sw1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // promotion ring; before the first slab the "previous slab's tail"
+        // is 0 * 0, which leaves the zero accumulators unchanged
+        f32x4 part[RING];
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            i32x8 fa_next = fa;
-            int sa_next = sa;
-            if (i + 1 < FM) {
-              fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
-              sa_next = (int)(Sw[(i + 1) * 16] >> sh);
-            }
+        for (int r = 0; r < RING; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float s_tail[LAG];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fa, acc[i][j], sbx, sa);
-            fa = fa_next;
-            sa = sa_next;
+        for (int l = 0; l < LAG; ++l) s_tail[l] = 0.f;
+
+        for (int it = 0; it < nkb; ++it) {
+          const int kb = kb_begin + it;
+          const int cur = it % STAGES, nxt = (it + 1) % STAGES;
+          const uint8_t* As = As0 + cur * STAGE;
+          // the slab's scales (FP32: row scales and block scale; UE8M0: packed words)
+          float sc[FM];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) sc[i] = *reinterpret_cast<const float*>(Ss0 + cur * STAGE + i * 16 * 4);
+          const float sb = *reinterpret_cast<const float*>(Sb0 + cur * STAGE);
+          float s[FM];
+          int sx[FM];
+          int sbx = 0;
+          if constexpr (E8M0) {
+            const int sh = 8 * (kb & 3);
+            sbx = (int)(__float_as_uint(sb) >> sh);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sx[i] = (int)(__float_as_uint(sc[i]) >> sh);
+          } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) s[i] = sc[i] * sb;
           }
-        } else if (wave_live) {
-          const uint8_t* As = lds + cur * STAGE + (wm * TM + r16) * 128;
-          const uint8_t* Bs = lds + cur * STAGE + A_BYTES + (wn * TN + r16) * 128;
-          const float* Ss = reinterpret_cast<const float*>(lds + cur * STAGE + A_BYTES + B_BYTES) + wm * TM + r16;
-          i32x8 fb[FN];
+          // acc += partial of MFMA u of this slab (u >= 0) or of the previous slab's tail (u < 0)
+          auto promote = [&](int u) {
+            if constexpr (!E8M0) {
+              const int v = u < 0 ? u + T : u;
+              const int ui = row_of(v), uj = col_of(v);
+              const float su = u < 0 ? s_tail[u + LAG] : s[ui];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) fb[j] = read_frag(Bs + j * 16 * 128, sw0, sw1);
-          // Flat sequence of the FM*FN MFMAs of this slab.  The partial of MFMA
-          // t is promoted right after MFMA t+2 is issued (3-deep ring), so the
-          // promotion FMAs run under the matrix core.
-          constexpr int T = FM * FN;
-          constexpr int RING = 3;
-          f32x4 part[RING];
-          float s_cur = Ss[0] * sb, s_prev = 0.f;
-          i32x8 fa = read_frag(As, sw0, sw1);
-          i32x8 fa_next = fa;
-          float s_next = s_cur;
+              for (int r = 0; r < 4; ++r) acc[ui][uj][r] = __builtin_fmaf(part[v % RING][r], su, acc[ui][uj][r]);
+            }
+          };
+
+          if (wave_live) {
 #pragma unroll
-          for (int t = 0; t < T + RING - 1; ++t) {
-            const int i = t / FN, j = t % FN;
-            if (t < T) {
-              if (j == 0 && i + 1 < FM) {
-                fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
-                s_next = Ss[(i + 1) * 16] * sb;
+            for (int t = 0; t < T1; ++t) {
+              const int i = t / FN, j = t % FN;
+              if (j == 0 && i + 1 < FIRST) fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
+              if (j == FN / 2 && i < HOLD) fh[i] = read_frag(As + (FIRST + i) * 16 * 128, sw0, sw1);
+              if constexpr (E8M0) {
+                acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fa, acc[i][j], sbx, sx[i]);
+              } else {
+                part[t % RING] = mfma_fp8_16x16x128(fb[j], fa);
               }
-              part[t % RING] = mfma_fp8_16x16x128(fb[j], fa);
+              promote(t - LAG);
+              if (j == FN - 1 && i + 1 < FIRST) fa = fa_next;
+              if (j == FN - 1) __builtin_amdgcn_sched_barrier(0);
             }
-            const int u = t - (RING - 1);  // MFMA whose partial is promoted now
-            if (u >= 0) {
-              const int ui = u / FN, uj = u % FN;
-              // s_cur is fragment i's scale, s_prev fragment i-1's (u is at most one fragment behind t)
-              const float su = (t >= T || ui == i) ? s_cur : s_prev;
+          }
+
+          wait_slab();  // slab it + 1 has landed (this wave's part of it)
+          stage_barrier();
+          const bool load_live = it + STAGES < nkb;
+          const SlabRsrc nr = slab_rsrc(kb + STAGES, load_live);
+          const uint8_t* An = As0 + nxt * STAGE;
+          const uint8_t* Bn = Bs0 + nxt * STAGE;
+          if (wave_live) {
+            // (after the last slab these reads of the next stage are stale and unused)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[ui][uj][r] = __builtin_fmaf(part[u % RING][r], su, acc[ui][uj][r]);
+            for (int t = T1; t < T; ++t) {
+              const int w = t - T1, j = w / HOLD, h = w % HOLD, i = FIRST + h;
+              if constexpr (E8M0) {
+                acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fh[h], acc[i][j], sbx, sx[i]);
+              } else {
+                part[t % RING] = mfma_fp8_16x16x128(fb[j], fh[h]);
+              }
+              promote(t - LAG);
+              if (w < LOADS) issue_load(nr, cur, w);
+              if (h == HOLD - 1) {
+                fb[j] = read_frag(Bn + j * 16 * 128, sw0, sw1);
+                if (j == 0) fa = read_frag(An, sw0, sw1);
+                __builtin_amdgcn_sched_barrier(0);
+              }
             }
-            if (t < T && j == FN - 1 && i + 1 < FM) {
-              fa = fa_next;
-              s_prev = s_cur;
-              s_cur = s_next;
+            if constexpr (!E8M0) {
+#pragma unroll
+              for (int l = 0; l < LAG; ++l) s_tail[l] = s[row_of(T - LAG + l)];
+            }
+          } else {
+#pragma unroll
+            for (int idx = 0; idx < (LOADS < P2 ? LOADS : P2); ++idx) issue_load(nr, cur, idx);
+          }
+#pragma unroll
+          for (int idx = P2; idx < LOADS; ++idx) issue_load(nr, cur, idx);
+        }
+        // promote the last slab's tail
+        if (wave_live) {
+#pragma unroll
+          for (int l = 0; l < LAG; ++l) {
+            if constexpr (!E8M0) {
+              const int v = T - LAG + l;
+              const int ui = row_of(v), uj = col_of(v);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[ui][uj][r] = __builtin_fmaf(part[v % RING][r], s_tail[l], acc[ui][uj][r]);
             }
           }
         }
@@ -482,10 +563,14 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         }
         continue;
       }
-      // Epilogue: D = C + acc, masked stores.
+      // Epilogue: D = C + acc, masked stores.  (The empty asm makes the row
+      // index opaque, so the row addresses are computed here instead of being
+      // hoisted above the K loop, where registers are scarce.)
+      int row0 = wrow0 + r16;
+      asm volatile("" : "+v"(row0));
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int gm = wrow0 + i * 16 + r16;
+        const int gm = row0 + i * 16;
         bool row_ok = gm < row_end;
         if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
         if (!row_ok) continue;
