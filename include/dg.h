@@ -286,6 +286,16 @@ int64_t dg_get_sf_aligned_size(int64_t mn);
 dg_status dg_set_num_cus(int num_cus);
 int dg_get_num_cus(void);
 
+/* Tuning knob: width of the 256-row output tiles the large-M kernels use.
+ * 0 (default; DG_TILE_N in the environment sets the initial value) picks per
+ * call among 256, 224 and 160 columns the width with the fewest workgroup
+ * rounds times tile width (narrower tiles even out the last round on the
+ * CUs, e.g. N = 7168); 256, 224 or 160 forces that width.  Other values ->
+ * DG_ERROR_INVALID_VALUE.  Process-wide; results agree to the stated
+ * tolerance whatever the width (the K order of every output is unchanged). */
+dg_status dg_set_tile_n(int tile_n);
+int dg_get_tile_n(void);
+
 /* Static text for a status code (never NULL). */
 const char* dg_status_string(dg_status s);
 

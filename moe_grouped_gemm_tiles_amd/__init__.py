@@ -18,7 +18,7 @@ as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
 * ``fp8_mqa_logits(q, (kv, kv_sf), weights, ks, ke, clean_logits, out)``
   (README "V3.2 MQA kernels for the indexer")
 * ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
-  ``set_num_cus(n)`` / ``get_num_cus()``
+  ``set_num_cus(n)`` / ``get_num_cus()``, ``set_tile_n(w)`` / ``get_tile_n()``
 
 The three M-side GEMMs take either FP32 scales or UE8M0 scales packed four
 per int32 along K (the README's "Interfaces > Notices" names both formats);
@@ -56,6 +56,8 @@ __all__ = [
     "get_sf_aligned_size",
     "set_num_cus",
     "get_num_cus",
+    "set_tile_n",
+    "get_tile_n",
     "library_path",
     "load_library",
 ]
@@ -95,6 +97,8 @@ _SIGNATURES = {
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
     "dg_get_num_cus": (_i32, []),
+    "dg_set_tile_n": (_i32, [_i32]),
+    "dg_get_tile_n": (_i32, []),
     "dg_status_string": (ctypes.c_char_p, [_i32]),
     "dg_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -440,3 +444,12 @@ def set_num_cus(n: int):
 
 def get_num_cus() -> int:
     return load_library().dg_get_num_cus()
+
+
+def set_tile_n(w: int):
+    """Force the width of the 256-row tiles (256, 224 or 160; 0 = automatic)."""
+    _check(load_library().dg_set_tile_n(w))
+
+
+def get_tile_n() -> int:
+    return load_library().dg_get_tile_n()

@@ -33,6 +33,7 @@ int g_device_cus[kMaxDevices] = {0};
 std::once_flag g_env_once;
 bool g_print_configs = false;
 int g_force_splits = 0;
+std::atomic<int> g_tile_n{0};  // forced width of the 256-row tiles (0 = automatic)
 
 void read_env() {
   std::call_once(g_env_once, [] {
@@ -40,6 +41,9 @@ void read_env() {
     g_print_configs = s && std::atoi(s) != 0;
     const char* f = std::getenv("DG_FORCE_SPLITS");
     g_force_splits = f ? std::atoi(f) : 0;
+    const char* tn = std::getenv("DG_TILE_N");
+    const int w = tn ? std::atoi(tn) : 0;
+    if (w == 256 || w == 224 || w == 160) g_tile_n.store(w);
     int expected = -1;
     const char* c = std::getenv("DG_NUM_CUS");
     const int v = c ? std::atoi(c) : 0;
@@ -72,14 +76,18 @@ inline int64_t dtype_size(dg_dtype t) { return t == DG_DTYPE_BF16 ? 2 : 4; }
 
 using KernelFn = void (*)(dg::Params);
 
-// Tile configurations.  LDS per workgroup = stages x ((BM + BN) x 128 B + BM x 4 B):
+// Tile configurations.  LDS per workgroup = stages x ((BM + BN) x 128 B + BM x 4 B
+// + B-scale words, rounded up to 256 B):
 //   256x256, 8 waves, 2 stages: 130 KiB (one workgroup per CU) -- large M and N
+//   256x224, 8 waves, 2 stages: 122 KiB (one per CU)            -- large M, N = 7 x 1024
+//   256x160, 8 waves, 2 stages: 106 KiB (one per CU)            -- large M, N like 2112
 //   128x128, 4 waves, 2 stages:  65 KiB (two per CU)           -- small grouped tiles
 //   128x64,  4 waves, 3 stages:  74 KiB (two per CU), split-K  -- dense 64 < M <= 128
 //    64x128, 4 waves, 3 stages:  73 KiB (two per CU), split-K  -- dense M <= 64
 // The split-K configurations stream B from HBM; two independent workgroups
 // per CU keep four slabs in flight per CU.
-enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x64 = 2, TILE_SK_64x128 = 3 };
+enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x64 = 2, TILE_SK_64x128 = 3, TILE_256x224 = 4,
+              TILE_256x160 = 5 };
 
 struct Cfg {
   TileId id;
@@ -87,6 +95,8 @@ struct Cfg {
 };
 
 constexpr Cfg kCfg256{TILE_256x256, 256, 256, 2, 4, 2, 1};
+constexpr Cfg kCfg256x224{TILE_256x224, 256, 224, 4, 2, 2, 1};
+constexpr Cfg kCfg256x160{TILE_256x160, 256, 160, 4, 2, 2, 1};
 constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
 constexpr Cfg kCfgSk128{TILE_SK_128x64, 128, 64, 2, 2, 3, 2};
 constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 3, 2};
@@ -131,6 +141,8 @@ KernelFn pick_tile(const Cfg& c, const Epi& e) {
     if (c.id == TILE_SK_64x128) return pick_out<64, 128, 1, 4, 3, MODE, E8M0>(e);
   }
   if (c.id == TILE_256x256) return pick_out<256, 256, 2, 4, 2, MODE, E8M0>(e);
+  if (c.id == TILE_256x224) return pick_out<256, 224, 4, 2, 2, MODE, E8M0>(e);
+  if (c.id == TILE_256x160) return pick_out<256, 160, 4, 2, 2, MODE, E8M0>(e);
   return pick_out<128, 128, 2, 2, 2, MODE, E8M0>(e);
 }
 
@@ -180,6 +192,32 @@ dg_status get_workspace(size_t bytes, hipStream_t stream, float** out) {
   }
   *out = static_cast<float*>(ent.first);
   return DG_SUCCESS;
+}
+
+// Width of the 256-row tiles: the candidate with the least (workgroup rounds x
+// tile width x relative cost per column) -- narrower tiles even out the last
+// round of tiles (N = 7168: 448 tiles of 256x256 on 256 CUs leave 1.75 rounds,
+// 512 tiles of 256x224 exactly 2) but re-read more LDS per MFMA.
+// `row_tiles` = 256-row tiles per N column of tiles (all groups together).
+Cfg choose_wide(int64_t row_tiles, int n, int slots) {
+  read_env();
+  const Cfg cands[3] = {kCfg256, kCfg256x224, kCfg256x160};
+  // time per tile column relative to 256x256 (measured on 8192x8192x16384)
+  const double col_cost[3] = {1.0, 1.11, 1.19};
+  Cfg best = kCfg256;
+  double best_cost = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const int forced = g_tile_n.load();
+    if (forced > 0 && cands[i].bn != forced) continue;
+    const int64_t tiles = row_tiles * cdiv(n, cands[i].bn);
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double cost = static_cast<double>(rounds) * cands[i].bn * col_cost[i];
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = cands[i];
+    }
+  }
+  return best;
 }
 
 // Split count for a skinny dense GEMM: minimise (workgroup rounds x slabs per
@@ -312,7 +350,10 @@ dg_status dense_impl(const void* a, int64_t lda, const void* sfa, int64_t ld_sfa
   p.num_groups = 1;
   if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
     return DG_ERROR_NOT_SUPPORTED;
-  const Cfg cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? kCfg256 : kCfg128);
+  int cus = 0;
+  st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  const Cfg cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? choose_wide(cdiv(m, 256), n, cus) : kCfg128);
   return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, e8m0, 1, stream);
 }
 
@@ -346,7 +387,10 @@ dg_status contiguous_impl(const void* a, const void* sfa, int64_t ld_sfa, const 
   p.k = k;
   p.num_groups = num_groups;
   if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
-  const Cfg cfg = n > 128 ? kCfg256 : kCfg128;
+  int cus = 0;
+  st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  const Cfg cfg = n > 128 ? choose_wide(cdiv(m_total, 256), n, cus) : kCfg128;
   return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, e8m0, 1, stream);
 }
 
@@ -383,7 +427,10 @@ dg_status masked_impl(const void* a, const void* sfa, int64_t ld_sfa, const void
   p.num_groups = num_groups;
   if (static_cast<int64_t>(k) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
   const int em = expected_m > 0 ? expected_m : m_max;
-  const Cfg cfg = (em > 128 && n > 128) ? kCfg256 : kCfg128;
+  int cus = 0;
+  st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  const Cfg cfg = (em > 128 && n > 128) ? choose_wide(static_cast<int64_t>(num_groups) * cdiv(em, 256), n, cus) : kCfg128;
   return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, e8m0, num_groups, stream);
 }
 
@@ -418,7 +465,10 @@ dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const 
   p.k = k_total;
   p.num_groups = num_groups;
   if (static_cast<int64_t>(k_total) * 256 >= (1ll << 31)) return DG_ERROR_NOT_SUPPORTED;
-  const Cfg cfg = (m > 128 && n > 128) ? kCfg256 : kCfg128;
+  int cus = 0;
+  st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  const Cfg cfg = (m > 128 && n > 128) ? choose_wide(static_cast<int64_t>(num_groups) * cdiv(m, 256), n, cus) : kCfg128;
   return launch<dg::MODE_KGROUP>(p, cfg, DG_DTYPE_FP32, c != nullptr, false, num_groups, stream);
 }
 
@@ -511,6 +561,18 @@ dg_status dg_set_num_cus(int num_cus) {
 int dg_get_num_cus(void) {
   read_env();
   return g_num_cus.load();
+}
+
+dg_status dg_set_tile_n(int tile_n) {
+  if (tile_n != 0 && tile_n != 256 && tile_n != 224 && tile_n != 160) return DG_ERROR_INVALID_VALUE;
+  read_env();
+  g_tile_n.store(tile_n);
+  return DG_SUCCESS;
+}
+
+int dg_get_tile_n(void) {
+  read_env();
+  return g_tile_n.load();
 }
 
 const char* dg_status_string(dg_status s) {

@@ -224,24 +224,40 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, SFA_BYTES = BM * 4;
-  constexpr int SFB_SLOTS = (BN + 127) / 128;  // B-scale words per slab: one per 128-column block of the tile
+  // A wave's columns may straddle two 128-column scale blocks when the tile
+  // width is not a multiple of 128 (or a wave's width does not divide 128).
+  constexpr bool STRADDLE = (BN % 128 != 0) || (128 % TN != 0);
+  // B-scale words per slab: one per 128-column block the tile can touch
+  constexpr int SFB_SLOTS = STRADDLE ? (BN + 127) / 128 + 1 : (BN + 127) / 128;
   constexpr int SFB_OFF = A_BYTES + B_BYTES + SFA_BYTES;
   // stages start on 256-byte boundaries, so every stage has the same bank phase
   constexpr int STAGE = (SFB_OFF + 4 * SFB_SLOTS + 255) / 256 * 256;
-  constexpr int A_LOADS = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per slab
-  constexpr int B_LOADS = B_BYTES / 1024 / NW;
+  // 1 KiB (8-row) direct loads per slab: A_TOTAL of A, B_TOTAL of B, split
+  // over the waves in blocks of A_LOADS / B_LOADS (the last waves may have fewer)
+  constexpr int A_TOTAL = BM / 8, B_TOTAL = BN / 8;
+  constexpr int A_LOADS = (A_TOTAL + NW - 1) / NW;
+  constexpr int B_LOADS = (B_TOTAL + NW - 1) / NW;
   constexpr int LOADS = A_LOADS + B_LOADS;
+  constexpr bool EVEN_LOADS = A_LOADS * NW == A_TOTAL && B_LOADS * NW == B_TOTAL;
   constexpr int SFA_LANES = BM / 4;  // lanes of wave 0 that stage the slab's row scales (16 B each)
-  // Slab schedule (see the K loop): the last HOLD fragment rows of a slab are
-  // multiplied after the slab's barrier; partial t is promoted after MFMA t + LAG.
-  constexpr int HOLD = 2, FIRST = FM - HOLD;
-  constexpr int T = FM * FN, T1 = FIRST * FN, P2 = HOLD * FN;
+  // Slab schedule (see the K loop).  The operand with fewer fragments per
+  // wave ("outer": B unless A has fewer) stays in registers for the whole
+  // slab; the other ("inner") is streamed.  The last HOLD inner fragments of
+  // a slab are multiplied after the slab's barrier; partial t is promoted
+  // after MFMA t + LAG.
+  constexpr bool A_OUTER = FM < FN;
+  constexpr int NO = A_OUTER ? FM : FN, NI = A_OUTER ? FN : FM;
+  constexpr int HOLD = 2, FIRST = NI - HOLD;
+  constexpr int T = FM * FN, T1 = FIRST * NO, P2 = HOLD * NO;
   constexpr int RING = 4, LAG = 3;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
-  static_assert(128 % TN == 0, "a wave's columns must lie in one 128-column scale block");
-  static_assert(FIRST >= HOLD && FN >= 2, "two-part slab schedule");
+  static_assert(TN <= 128, "a wave's columns touch at most two 128-column scale blocks");
+  static_assert(FIRST >= HOLD && NO >= 2, "two-part slab schedule");
   static_assert(T % RING == 0 && LAG < RING && LAG <= P2, "promotion ring");
-  static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "loads must split evenly");
+  static_assert(BM % 8 == 0 && BN % 8 == 0, "loads cover 8 rows");
+  // uneven splits give the waves different load counts per slab, which only
+  // the double-buffered schedule (it waits for all loads) tolerates
+  static_assert(EVEN_LOADS || STAGES == 2, "uneven load split needs two stages");
   static_assert(SFA_LANES >= 1 && SFA_LANES <= 64 && SFA_LANES * 16 == SFA_BYTES, "sfa staging");
   static_assert(NW >= 2, "the A and B scale loads ride on different waves");
   static_assert(MODE != MODE_CONTIG || BM == 128 || BM == 256, "contiguous tiles cover one or two 128-row blocks");
@@ -331,6 +347,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       const int64_t a_rows = p.m - m0, b_rows = p.n - n0;
 
       // per-lane offsets of this wave's direct loads (fixed over K)
+      // (loads of a wave past A_TOTAL / B_TOTAL are not issued)
       uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
       for (int i = 0; i < A_LOADS; ++i)
@@ -367,9 +384,11 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       auto issue_load = [&](const SlabRsrc& r, int stage, int idx) {
         uint8_t* base = lds + stage * STAGE;
         if (idx < A_LOADS) {
-          load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
+          if (EVEN_LOADS || wave * A_LOADS + idx < A_TOTAL)
+            load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
         } else {
-          load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
+          if (EVEN_LOADS || wave * B_LOADS + idx - A_LOADS < B_TOTAL)
+            load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
         }
         if (idx == 0) {
           const int q = E8M0 ? (r.kb >> 2) : r.kb;  // scale row (A) / column (B) of the slab
@@ -413,9 +432,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       // the columns free up.  No LDS latency and no burst of loads sits at the
       // barrier.  Each slab's FP32 promotion trails its MFMAs by LAG and
       // carries across the slab boundary.
-      // fragment row / column of the slab's MFMA t
-      auto row_of = [](int t) { return t < T1 ? t / FN : FIRST + (t - T1) % HOLD; };
-      auto col_of = [](int t) { return t < T1 ? t % FN : (t - T1) / HOLD; };
+      // inner / outer fragment of the slab's MFMA t (part 1: inner-major over
+      // the streamed fragments, part 2: outer-major over the held ones), and
+      // the output fragment row / column they give
+      auto inner_of = [](int t) { return t < T1 ? t / NO : FIRST + (t - T1) % HOLD; };
+      auto outer_of = [](int t) { return t < T1 ? t % NO : (t - T1) / HOLD; };
+      auto row_of = [&](int t) { return A_OUTER ? outer_of(t) : inner_of(t); };
+      auto col_of = [&](int t) { return A_OUTER ? inner_of(t) : outer_of(t); };
       if (nkb > 0) {
 #pragma unroll
         for (int i = 0; i < STAGES - 1; ++i) issue_slab(kb_begin + i, i, i < nkb);
@@ -425,18 +448,24 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 
         const uint8_t* As0 = lds + (wm * TM + r16) * 128;
         const uint8_t* Bs0 = lds + A_BYTES + (wn * TN + r16) * 128;
+        const uint8_t* Is0 = A_OUTER ? Bs0 : As0;  // inner operand rows
+        const uint8_t* Os0 = A_OUTER ? As0 : Bs0;  // outer operand rows
         const uint8_t* Ss0 = lds + A_BYTES + B_BYTES + (wm * TM + r16) * 4;
-        const uint8_t* Sb0 = lds + SFB_OFF + ((wn * TN) >> 7) * 4;
+        // this wave's first scale block (slot of the staged words) and, when
+        // its columns straddle two blocks, the number of its fragments in the first
+        const int wcol = n0 + wn * TN;
+        const uint8_t* Sb0 = lds + SFB_OFF + ((wcol >> 7) - (n0 >> 7)) * 4;
+        const int jsplit = STRADDLE ? min(FN, (128 - (wcol & 127)) >> 4) : FN;
 
         // slab 0's fragments, read in the order part 2 reads the next slab's,
         // so that the waits at the loop head agree on both paths into it
-        i32x8 fb[FN], fh[HOLD];
-        fb[0] = read_frag(Bs0, sw0, sw1);
-        i32x8 fa = read_frag(As0, sw0, sw1), fa_next = fa;
+        i32x8 fo[NO], fh[HOLD];
+        fo[0] = read_frag(Os0, sw0, sw1);
+        i32x8 fi = read_frag(Is0, sw0, sw1), fi_next = fi;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 1; j < FN; ++j) {
-          fb[j] = read_frag(Bs0 + j * 16 * 128, sw0, sw1);
+        for (int o = 1; o < NO; ++o) {
+          fo[o] = read_frag(Os0 + o * 16 * 128, sw0, sw1);
           __builtin_amdgcn_sched_barrier(0);
         }
         // promotion ring; before the first slab the "previous slab's tail"
@@ -451,30 +480,47 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         for (int it = 0; it < nkb; ++it) {
           const int kb = kb_begin + it;
           const int cur = it % STAGES, nxt = (it + 1) % STAGES;
-          const uint8_t* As = As0 + cur * STAGE;
+          const uint8_t* Is = Is0 + cur * STAGE;
           // the slab's scales (FP32: row scales and block scale; UE8M0: packed words)
           float sc[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) sc[i] = *reinterpret_cast<const float*>(Ss0 + cur * STAGE + i * 16 * 4);
           const float sb = *reinterpret_cast<const float*>(Sb0 + cur * STAGE);
-          float s[FM];
+          const float sb1 = STRADDLE ? *reinterpret_cast<const float*>(Sb0 + 4 + cur * STAGE) : sb;
+          // s / s1: promotion scales of the wave's fragments in its first / second block
+          float s[FM], s1[FM];
           int sx[FM];
-          int sbx = 0;
+          int sbx = 0, sbx1 = 0;
           if constexpr (E8M0) {
             const int sh = 8 * (kb & 3);
             sbx = (int)(__float_as_uint(sb) >> sh);
+            sbx1 = (int)(__float_as_uint(sb1) >> sh);
 #pragma unroll
             for (int i = 0; i < FM; ++i) sx[i] = (int)(__float_as_uint(sc[i]) >> sh);
           } else {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) s[i] = sc[i] * sb;
+            for (int i = 0; i < FM; ++i) {
+              s[i] = sc[i] * sb;
+              if (STRADDLE) s1[i] = sc[i] * sb1;
+            }
           }
+          // MFMA t of the slab with operands (outer fragment x, inner fragment y)
+          auto mma = [&](int t, const i32x8& x, const i32x8& y) {
+            const int i = row_of(t), j = col_of(t);
+            const i32x8& fbv = A_OUTER ? y : x;  // B fragment (first operand)
+            const i32x8& fav = A_OUTER ? x : y;  // A fragment
+            if constexpr (E8M0) {
+              acc[i][j] = mfma_fp8_16x16x128_e8m0(fbv, fav, acc[i][j], (STRADDLE && j >= jsplit) ? sbx1 : sbx, sx[i]);
+            } else {
+              part[t % RING] = mfma_fp8_16x16x128(fbv, fav);
+            }
+          };
           // acc += partial of MFMA u of this slab (u >= 0) or of the previous slab's tail (u < 0)
           auto promote = [&](int u) {
             if constexpr (!E8M0) {
               const int v = u < 0 ? u + T : u;
               const int ui = row_of(v), uj = col_of(v);
-              const float su = u < 0 ? s_tail[u + LAG] : s[ui];
+              const float su = u < 0 ? s_tail[u + LAG] : ((STRADDLE && uj >= jsplit) ? s1[ui] : s[ui]);
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[ui][uj][r] = __builtin_fmaf(part[v % RING][r], su, acc[ui][uj][r]);
             }
@@ -483,17 +529,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           if (wave_live) {
 #pragma unroll
             for (int t = 0; t < T1; ++t) {
-              const int i = t / FN, j = t % FN;
-              if (j == 0 && i + 1 < FIRST) fa_next = read_frag(As + (i + 1) * 16 * 128, sw0, sw1);
-              if (j == FN / 2 && i < HOLD) fh[i] = read_frag(As + (FIRST + i) * 16 * 128, sw0, sw1);
-              if constexpr (E8M0) {
-                acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fa, acc[i][j], sbx, sx[i]);
-              } else {
-                part[t % RING] = mfma_fp8_16x16x128(fb[j], fa);
-              }
+              const int n = t / NO, o = t % NO;
+              if (o == 0 && n + 1 < FIRST) fi_next = read_frag(Is + (n + 1) * 16 * 128, sw0, sw1);
+              if (o == NO / 2 && n < HOLD) fh[n] = read_frag(Is + (FIRST + n) * 16 * 128, sw0, sw1);
+              mma(t, fo[o], fi);
               promote(t - LAG);
-              if (j == FN - 1 && i + 1 < FIRST) fa = fa_next;
-              if (j == FN - 1) __builtin_amdgcn_sched_barrier(0);
+              if (o == NO - 1 && n + 1 < FIRST) fi = fi_next;
+              if (o == NO - 1) __builtin_amdgcn_sched_barrier(0);
             }
           }
 
@@ -501,29 +543,28 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           stage_barrier();
           const bool load_live = it + STAGES < nkb;
           const SlabRsrc nr = slab_rsrc(kb + STAGES, load_live);
-          const uint8_t* An = As0 + nxt * STAGE;
-          const uint8_t* Bn = Bs0 + nxt * STAGE;
+          const uint8_t* In = Is0 + nxt * STAGE;
+          const uint8_t* On = Os0 + nxt * STAGE;
           if (wave_live) {
             // (after the last slab these reads of the next stage are stale and unused)
 #pragma unroll
             for (int t = T1; t < T; ++t) {
-              const int w = t - T1, j = w / HOLD, h = w % HOLD, i = FIRST + h;
-              if constexpr (E8M0) {
-                acc[i][j] = mfma_fp8_16x16x128_e8m0(fb[j], fh[h], acc[i][j], sbx, sx[i]);
-              } else {
-                part[t % RING] = mfma_fp8_16x16x128(fb[j], fh[h]);
-              }
+              const int w = t - T1, o = w / HOLD, h = w % HOLD;
+              mma(t, fo[o], fh[h]);
               promote(t - LAG);
               if (w < LOADS) issue_load(nr, cur, w);
               if (h == HOLD - 1) {
-                fb[j] = read_frag(Bn + j * 16 * 128, sw0, sw1);
-                if (j == 0) fa = read_frag(An, sw0, sw1);
+                fo[o] = read_frag(On + o * 16 * 128, sw0, sw1);
+                if (o == 0) fi = read_frag(In, sw0, sw1);
                 __builtin_amdgcn_sched_barrier(0);
               }
             }
             if constexpr (!E8M0) {
 #pragma unroll
-              for (int l = 0; l < LAG; ++l) s_tail[l] = s[row_of(T - LAG + l)];
+              for (int l = 0; l < LAG; ++l) {
+                const int v = T - LAG + l;
+                s_tail[l] = (STRADDLE && col_of(v) >= jsplit) ? s1[row_of(v)] : s[row_of(v)];
+              }
             }
           } else {
 #pragma unroll

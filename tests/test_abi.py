@@ -50,6 +50,10 @@ def test_utilities(lib):
     assert lib.dg_set_num_cus(-1) == INVALID
     assert lib.dg_set_num_cus(64) == 0 and lib.dg_get_num_cus() == 64
     assert lib.dg_set_num_cus(0) == 0 and lib.dg_get_num_cus() == 0
+    for bad in (-1, 1, 128, 192, 512):
+        assert lib.dg_set_tile_n(bad) == INVALID
+    for w in (256, 224, 160, 0):
+        assert lib.dg_set_tile_n(w) == 0 and lib.dg_get_tile_n() == w
     for s in range(5):
         assert lib.dg_status_string(s)
     assert lib.dg_status_string(99) == b"DG_UNKNOWN_STATUS"
