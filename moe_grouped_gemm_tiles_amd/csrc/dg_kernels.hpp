@@ -285,135 +285,202 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   const int ld_row = lane >> 3;
   const int ld_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
 
+  // Work units: (tile, pass); a contiguous tile whose two 128-row halves
+  // belong to different groups takes one pass per group.
+  struct Unit {
+    int tile, pass, passes;  // tile < 0: no unit
+    int g, g0, g1, m0, n0, row_end, kb_begin, kb_end, split;
+  };
+  // The unit (tile, pass), or the first valid one at or after it in this
+  // workgroup's tile sequence.
+  auto find_unit = [&](int tile, int pass) {
+    Unit u;
+    u.tile = -1;
+    for (; tile < p.num_tiles; tile += gridDim.x, pass = 0) {
+      int g = 0, t = tile, split = 0;
+      if (MODE == MODE_MASKED || MODE == MODE_KGROUP) {
+        g = t / tiles_mn;
+        t -= g * tiles_mn;
+      }
+      if (SPLIT) {
+        split = t / tiles_mn;
+        t -= split * tiles_mn;
+      }
+      int kb_begin = SPLIT ? split * p.slabs_per_split : 0;
+      int kb_end = SPLIT ? min(KB, kb_begin + p.slabs_per_split) : KB;
+      if (MODE == MODE_KGROUP) {
+        // group g's K blocks start after the blocks of groups 0..g-1; sizes are
+        // device data, so they are clamped into [0, KB] rather than trusted
+        int off = 0;
+        for (int h = 0; h < g; ++h) off += max(p.grp[h], 0) >> 7;
+        kb_begin = min(off, KB);
+        kb_end = min(kb_begin + (max(p.grp[g], 0) >> 7), KB);
+      }
+      int mb, nb;
+      raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
+      const int m0 = mb * BM, n0 = nb * BN;
+      // groups served by this tile (contiguous: one per 128-row half)
+      int row_end = p.m, g0 = 0, g1 = 0, passes = 1;
+      if (MODE == MODE_MASKED) {
+        const int mm = min(max(p.grp[g], 0), p.m);
+        if (m0 >= mm) continue;
+        row_end = mm;
+      } else if (MODE == MODE_CONTIG) {
+        g0 = p.grp[m0];
+        g1 = (BM == 256 && m0 + 128 < p.m) ? p.grp[m0 + 128] : -1;
+        if (g0 < 0 || g0 >= p.num_groups) g0 = -1;
+        if (g1 < 0 || g1 >= p.num_groups) g1 = -1;
+        if (g0 < 0 && g1 < 0) continue;
+        if (g0 < 0) g0 = g1;
+        if (g1 < 0) g1 = g0;
+        passes = (g0 == g1) ? 1 : 2;
+        g = pass == 0 ? g0 : g1;
+      }
+      u.tile = tile;
+      u.pass = pass;
+      u.passes = passes;
+      u.g = g;
+      u.g0 = g0;
+      u.g1 = g1;
+      u.m0 = m0;
+      u.n0 = n0;
+      u.row_end = row_end;
+      u.kb_begin = kb_begin;
+      u.kb_end = kb_end;
+      u.split = split;
+      break;
+    }
+    return u;
+  };
+  auto next_unit = [&](const Unit& u) {
+    return u.pass + 1 < u.passes ? find_unit(u.tile, u.pass + 1) : find_unit(u.tile + (int)gridDim.x, 0);
+  };
+
+  // Operand bases of a unit.
+  struct Src {
+    const uint8_t* A;
+    const float* SFA;
+    const uint8_t* B;
+    const float* SFB;
+    int64_t a_rows, b_rows;
+    uint32_t sfb_off;
+  };
+  constexpr bool B_GROUPED = MODE == MODE_CONTIG || MODE == MODE_MASKED;
+  const int sfb_row = E8M0 ? KQ : KB;
+  const uint32_t sfb_bytes = (uint32_t)(NBLK * sfb_row) * 4;
+  auto src_of = [&](const Unit& u) {
+    Src r;
+    r.A = p.a + (MODE == MODE_MASKED ? (int64_t)u.g * p.a_gs : 0) + (int64_t)u.m0 * p.lda;
+    r.SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * p.sfa_gs : 0) + u.m0;
+    r.B = p.b + (B_GROUPED ? (int64_t)u.g * p.b_gs : 0) + (int64_t)u.n0 * p.ldb;
+    r.SFB = p.sfb + (B_GROUPED ? (int64_t)u.g * p.sfb_gs : 0);
+    r.a_rows = p.m - u.m0;
+    r.b_rows = p.n - u.n0;
+    // B-scale words staged with each slab: slot v holds block min(n0/128 + v, NBLK-1)
+    // (clamped: columns past N are never stored)
+    r.sfb_off = (uint32_t)(min((u.n0 >> 7) + lane, NBLK - 1) * sfb_row) * 4;
+    return r;
+  };
+
+  // per-lane offsets of this wave's direct loads (fixed over K and tiles)
+  // (loads of a wave past A_TOTAL / B_TOTAL are not issued)
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) a_off[i] = (uint32_t)(((wave * A_LOADS + i) * 8 + ld_row) * p.lda) + ld_chunk;
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) b_off[i] = (uint32_t)(((wave * B_LOADS + i) * 8 + ld_row) * p.ldb) + ld_chunk;
+
+  // Descriptors of slab kb; a slab past the unit's K range gets empty
+  // descriptors, so its loads (issued anyway, which keeps the wait counts
+  // fixed) fetch nothing and write zeros.
+  struct SlabRsrc {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int kb;
+    bool live;
+  };
+  auto slab_rsrc = [&](const Src& sr, int kb, bool live) {
+    SlabRsrc r;
+    r.ra = make_rsrc(sr.A + kb * 128, live ? clamp_bytes(sr.a_rows * p.lda - kb * 128) : 0u);
+    r.rb = make_rsrc(sr.B + kb * 128, live ? clamp_bytes(sr.b_rows * p.ldb - kb * 128) : 0u);
+    r.kb = kb;
+    r.live = live;
+    return r;
+  };
+  // Load idx of the wave's LOADS direct loads of a slab into `stage`
+  // (idx < A_LOADS: A rows, else B rows); idx 0 also stages the scales
+  // (A row scales on wave 0, B block scales on the last wave).
+  auto issue_load = [&](const Src& sr, const SlabRsrc& r, int stage, int idx) {
+    uint8_t* base = lds + stage * STAGE;
+    if (idx < A_LOADS) {
+      if (EVEN_LOADS || wave * A_LOADS + idx < A_TOTAL)
+        load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
+    } else {
+      if (EVEN_LOADS || wave * B_LOADS + idx - A_LOADS < B_TOTAL)
+        load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
+    }
+    if (idx == 0) {
+      const int q = E8M0 ? (r.kb >> 2) : r.kb;  // scale row (A) / column (B) of the slab
+      if (wave == 0 && lane < SFA_LANES)
+        load_to_lds16(make_rsrc(sr.SFA + (int64_t)q * p.ld_sfa, r.live ? clamp_bytes(sr.a_rows * 4) : 0u),
+                      base + A_BYTES + B_BYTES, lane * 16);
+      if (wave == NW - 1 && lane < SFB_SLOTS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(sr.SFB + q, r.live ? clamp_bytes((int64_t)sfb_bytes - 4 * q) : 0u),
+                                                 (lds_ptr_t)(base + SFB_OFF), 4, sr.sfb_off, 0, 0, 0);
+    }
+  };
+  auto issue_slab = [&](const Src& sr, int kb, int stage, bool live) {
+    const SlabRsrc r = slab_rsrc(sr, kb, live);
+#pragma unroll
+    for (int idx = 0; idx < LOADS; ++idx) issue_load(sr, r, stage, idx);
+  };
+  // Wait until this wave's loads of the slab STAGES-2 slabs before the
+  // newest issued one have landed (waves 0 and NW-1 issue one more load per slab).
+  auto wait_slab = [&]() {
+    if (wave == 0 || wave == NW - 1) {
+      wait_vmcnt<(STAGES - 2) * (LOADS + 1)>();
+    } else {
+      wait_vmcnt<(STAGES - 2) * LOADS>();
+    }
+  };
+
+  // Cross-unit prefetch (two stages only): once a unit's K loop is done, the
+  // first two slabs of the next unit are issued before the unit's epilogue,
+  // so their latency hides behind the stores.  When the epilogue is known to
+  // issue exactly EPI_STORES stores and nothing else (full tile, no C, no
+  // group-id reads), the next unit's first waits let those stores stay in
+  // flight: loads and stores share the vector-memory counter, so the wait for
+  // slab 0 allows (fewest loads per slab of any wave) + EPI_STORES newer ones,
+  // and the wait for slab 1 allows EPI_STORES.
+  constexpr bool XPRE = STAGES == 2;
+  constexpr int EPI_STORES = FM * FN;
+  constexpr int L_MIN = [] {
+    int lmin = 1 << 20;
+    for (int w = 0; w < NW; ++w) {
+      const int na = A_TOTAL - w * A_LOADS, nb = B_TOTAL - w * B_LOADS;
+      const int l = (na < 0 ? 0 : (na > A_LOADS ? A_LOADS : na)) + (nb < 0 ? 0 : (nb > B_LOADS ? B_LOADS : nb));
+      lmin = l < lmin ? l : lmin;
+    }
+    return lmin;
+  }();
+  static_assert(!XPRE || L_MIN + EPI_STORES < 64, "vmcnt range");
+  constexpr bool EPI_COUNTED = !HAS_C && MODE != MODE_CONTIG;
+
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
-  for (int tile = vb; tile < p.num_tiles; tile += gridDim.x) {
-    int g = 0, t = tile, split = 0;
-    if (MODE == MODE_MASKED || MODE == MODE_KGROUP) {
-      g = t / tiles_mn;
-      t -= g * tiles_mn;
-    }
-    if (SPLIT) {
-      split = t / tiles_mn;
-      t -= split * tiles_mn;
-    }
-    int kb_begin = SPLIT ? split * p.slabs_per_split : 0;
-    int kb_end = SPLIT ? min(KB, kb_begin + p.slabs_per_split) : KB;
-    if (MODE == MODE_KGROUP) {
-      // group g's K blocks start after the blocks of groups 0..g-1; sizes are
-      // device data, so they are clamped into [0, KB] rather than trusted
-      int off = 0;
-      for (int h = 0; h < g; ++h) off += max(p.grp[h], 0) >> 7;
-      kb_begin = min(off, KB);
-      kb_end = min(kb_begin + (max(p.grp[g], 0) >> 7), KB);
-    }
-    const int nkb = kb_end - kb_begin;
-    int mb, nb;
-    raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
-    const int m0 = mb * BM, n0 = nb * BN;
-
-    // Groups served by this tile (contiguous: one per 128-row half).
-    int row_end = p.m;
-    int g_half[2] = {0, 0};
-    int passes = 1;
-    if (MODE == MODE_MASKED) {
-      const int mm = min(max(p.grp[g], 0), p.m);
-      if (m0 >= mm) continue;
-      row_end = mm;
-    } else if (MODE == MODE_CONTIG) {
-      int g0 = p.grp[m0];
-      int g1 = (BM == 256 && m0 + 128 < p.m) ? p.grp[m0 + 128] : -1;
-      if (g0 < 0 || g0 >= p.num_groups) g0 = -1;
-      if (g1 < 0 || g1 >= p.num_groups) g1 = -1;
-      if (g0 < 0 && g1 < 0) continue;
-      if (g0 < 0) g0 = g1;
-      if (g1 < 0) g1 = g0;
-      g_half[0] = g0;
-      g_half[1] = g1;
-      passes = (g0 == g1) ? 1 : 2;
-    }
-
-    for (int pass = 0; pass < passes; ++pass) {
-      if (MODE == MODE_CONTIG) g = g_half[pass];
+  Unit u = find_unit(vb, 0), nx;
+  int pre = 0;  // 0: nothing prefetched; 1: slabs 0, 1 prefetched, stores uncounted; 2: counted
+  while (u.tile >= 0) {
+    int pre_next = 0;
+    {
+      const int g = u.g, m0 = u.m0, n0 = u.n0, row_end = u.row_end;
+      const int kb_begin = u.kb_begin, kb_end = u.kb_end;
+      const int nkb = kb_end - kb_begin;
+      const int g_half[2] = {u.g0, u.g1};
       // rows this wave computes: [m0 + wm*TM, +TM); skip waves with no live rows
       const int wrow0 = m0 + wm * TM;
       bool wave_live = wrow0 < row_end;
       if (MODE == MODE_CONTIG && BM == 256) wave_live = wave_live && (g_half[(wm * TM) >> 7] == g);
-
-      constexpr bool B_GROUPED = MODE == MODE_CONTIG || MODE == MODE_MASKED;
-      const uint8_t* A = p.a + (MODE == MODE_MASKED ? (int64_t)g * p.a_gs : 0) + (int64_t)m0 * p.lda;
-      const float* SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)g * p.sfa_gs : 0) + m0;
-      const uint8_t* B = p.b + (B_GROUPED ? (int64_t)g * p.b_gs : 0) + (int64_t)n0 * p.ldb;
-      const float* SFB = p.sfb + (B_GROUPED ? (int64_t)g * p.sfb_gs : 0);
-      const int64_t a_rows = p.m - m0, b_rows = p.n - n0;
-
-      // per-lane offsets of this wave's direct loads (fixed over K)
-      // (loads of a wave past A_TOTAL / B_TOTAL are not issued)
-      uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i)
-        a_off[i] = (uint32_t)(((wave * A_LOADS + i) * 8 + ld_row) * p.lda) + ld_chunk;
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        b_off[i] = (uint32_t)(((wave * B_LOADS + i) * 8 + ld_row) * p.ldb) + ld_chunk;
-
-      // B-scale words staged with each slab: slot u holds block min(n0/128 + u, NBLK-1)
-      // (clamped: columns past N are never stored)
-      const int sfb_row = E8M0 ? KQ : KB;
-      const uint32_t sfb_off = (uint32_t)(min((n0 >> 7) + lane, NBLK - 1) * sfb_row) * 4;
-      const uint32_t sfb_bytes = (uint32_t)(NBLK * sfb_row) * 4;
-
-      // Descriptors of slab kb; a slab past the tile's K range gets empty
-      // descriptors, so its loads (issued anyway, which keeps the wait counts
-      // fixed) fetch nothing and write zeros.
-      struct SlabRsrc {
-        __amdgpu_buffer_rsrc_t ra, rb;
-        int kb;
-        bool live;
-      };
-      auto slab_rsrc = [&](int kb, bool live) {
-        SlabRsrc r;
-        r.ra = make_rsrc(A + kb * 128, live ? clamp_bytes(a_rows * p.lda - kb * 128) : 0u);
-        r.rb = make_rsrc(B + kb * 128, live ? clamp_bytes(b_rows * p.ldb - kb * 128) : 0u);
-        r.kb = kb;
-        r.live = live;
-        return r;
-      };
-      // Load idx of the wave's LOADS direct loads of a slab into `stage`
-      // (idx < A_LOADS: A rows, else B rows); idx 0 also stages the scales
-      // (A row scales on wave 0, B block scales on the last wave).
-      auto issue_load = [&](const SlabRsrc& r, int stage, int idx) {
-        uint8_t* base = lds + stage * STAGE;
-        if (idx < A_LOADS) {
-          if (EVEN_LOADS || wave * A_LOADS + idx < A_TOTAL)
-            load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
-        } else {
-          if (EVEN_LOADS || wave * B_LOADS + idx - A_LOADS < B_TOTAL)
-            load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
-        }
-        if (idx == 0) {
-          const int q = E8M0 ? (r.kb >> 2) : r.kb;  // scale row (A) / column (B) of the slab
-          if (wave == 0 && lane < SFA_LANES)
-            load_to_lds16(make_rsrc(SFA + (int64_t)q * p.ld_sfa, r.live ? clamp_bytes(a_rows * 4) : 0u),
-                          base + A_BYTES + B_BYTES, lane * 16);
-          if (wave == NW - 1 && lane < SFB_SLOTS)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(SFB + q, r.live ? clamp_bytes((int64_t)sfb_bytes - 4 * q) : 0u),
-                                                     (lds_ptr_t)(base + SFB_OFF), 4, sfb_off, 0, 0, 0);
-        }
-      };
-      auto issue_slab = [&](int kb, int stage, bool live) {
-        const SlabRsrc r = slab_rsrc(kb, live);
-#pragma unroll
-        for (int idx = 0; idx < LOADS; ++idx) issue_load(r, stage, idx);
-      };
-      // Wait until this wave's loads of the slab STAGES-2 slabs before the
-      // newest issued one have landed (waves 0 and NW-1 issue one more load per slab).
-      auto wait_slab = [&]() {
-        if (wave == 0 || wave == NW - 1) {
-          wait_vmcnt<(STAGES - 2) * (LOADS + 1)>();
-        } else {
-          wait_vmcnt<(STAGES - 2) * LOADS>();
-        }
-      };
+      const Src sr = src_of(u);
+      (void)g;
 
       f32x4 acc[FM][FN];
 #pragma unroll
@@ -440,11 +507,17 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       auto row_of = [&](int t) { return A_OUTER ? outer_of(t) : inner_of(t); };
       auto col_of = [&](int t) { return A_OUTER ? inner_of(t) : outer_of(t); };
       if (nkb > 0) {
+        if (pre == 0) {
 #pragma unroll
-        for (int i = 0; i < STAGES - 1; ++i) issue_slab(kb_begin + i, i, i < nkb);
-        wait_slab();
+          for (int i = 0; i < STAGES - 1; ++i) issue_slab(sr, kb_begin + i, i, i < nkb);
+          wait_slab();
+        } else if (pre == 2) {
+          wait_vmcnt<(XPRE ? L_MIN + EPI_STORES : 0)>();  // slab 0 landed; slab 1 and the stores may not have
+        } else {
+          wait_vmcnt<0>();
+        }
         stage_barrier();
-        issue_slab(kb_begin + STAGES - 1, STAGES - 1, STAGES - 1 < nkb);
+        if (pre == 0) issue_slab(sr, kb_begin + STAGES - 1, STAGES - 1, STAGES - 1 < nkb);
 
         const uint8_t* As0 = lds + (wm * TM + r16) * 128;
         const uint8_t* Bs0 = lds + A_BYTES + (wn * TN + r16) * 128;
@@ -539,10 +612,16 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             }
           }
 
-          wait_slab();  // slab it + 1 has landed (this wave's part of it)
+          // slab it + 1 has landed (this wave's part of it); right after a
+          // counted prefetch only the previous epilogue's stores are newer
+          if (XPRE && it == 0 && pre == 2) {
+            wait_vmcnt<(XPRE ? EPI_STORES : 0)>();
+          } else {
+            wait_slab();
+          }
           stage_barrier();
           const bool load_live = it + STAGES < nkb;
-          const SlabRsrc nr = slab_rsrc(kb + STAGES, load_live);
+          const SlabRsrc nr = slab_rsrc(sr, kb + STAGES, load_live);
           const uint8_t* In = Is0 + nxt * STAGE;
           const uint8_t* On = Os0 + nxt * STAGE;
           if (wave_live) {
@@ -552,7 +631,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
               const int w = t - T1, o = w / HOLD, h = w % HOLD;
               mma(t, fo[o], fh[h]);
               promote(t - LAG);
-              if (w < LOADS) issue_load(nr, cur, w);
+              if (w < LOADS) issue_load(sr, nr, cur, w);
               if (h == HOLD - 1) {
                 fo[o] = read_frag(On + o * 16 * 128, sw0, sw1);
                 if (o == 0) fi = read_frag(In, sw0, sw1);
@@ -568,10 +647,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             }
           } else {
 #pragma unroll
-            for (int idx = 0; idx < (LOADS < P2 ? LOADS : P2); ++idx) issue_load(nr, cur, idx);
+            for (int idx = 0; idx < (LOADS < P2 ? LOADS : P2); ++idx) issue_load(sr, nr, cur, idx);
           }
 #pragma unroll
-          for (int idx = P2; idx < LOADS; ++idx) issue_load(nr, cur, idx);
+          for (int idx = P2; idx < LOADS; ++idx) issue_load(sr, nr, cur, idx);
         }
         // promote the last slab's tail
         if (wave_live) {
@@ -586,45 +665,60 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           }
         }
       }
-      stage_barrier();  // all LDS reads of this tile are done before the next tile's loads
+      stage_barrier();  // all LDS reads of this unit are done before the next unit's loads
 
-      if (!wave_live) continue;
-      if (SPLIT) {
-        // FP32 partial of this K range; the reduce kernel adds the ranges in order.
-        float* W = p.ws + (int64_t)split * p.m * p.ldw;
+      // next unit: its first two slabs go out before this unit's stores
+      nx = next_unit(u);
+      if (XPRE && nx.tile >= 0 && nx.kb_end > nx.kb_begin) {
+        const Src ns = src_of(nx);
+        issue_slab(ns, nx.kb_begin, 0, true);
+        issue_slab(ns, nx.kb_begin + 1, 1, nx.kb_begin + 1 < nx.kb_end);
+        const bool counted = EPI_COUNTED && m0 + BM <= row_end && n0 + BN <= p.n;
+        pre_next = counted ? 2 : 1;
+        asm volatile("" ::: "memory");  // the prefetch precedes every store below
+      }
+
+      if (wave_live) {
+        if (SPLIT) {
+          // FP32 partial of this K range; the reduce kernel adds the ranges in order.
+          float* W = p.ws + (int64_t)u.split * p.m * p.ldw;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int gm = wrow0 + i * 16 + r16;
-          if (gm >= p.m) continue;
+          for (int i = 0; i < FM; ++i) {
+            const int gm = wrow0 + i * 16 + r16;
+            if (gm >= p.m) continue;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int gn = n0 + wn * TN + j * 16 + 4 * q4;
-            if (gn < p.n) *reinterpret_cast<f32x4*>(W + (int64_t)gm * p.ldw + gn) = acc[i][j];
+            for (int j = 0; j < FN; ++j) {
+              const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+              if (gn < p.n) *reinterpret_cast<f32x4*>(W + (int64_t)gm * p.ldw + gn) = acc[i][j];
+            }
+          }
+        } else {
+          // Epilogue: D = C + acc, masked stores.  (The empty asm makes the row
+          // index opaque, so the row addresses are computed here instead of being
+          // hoisted above the K loop, where registers are scarce.)
+          int row0 = wrow0 + r16;
+          asm volatile("" : "+v"(row0));
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int gm = row0 + i * 16;
+            bool row_ok = gm < row_end;
+            if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
+            if (!row_ok) continue;
+            const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+            const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+              if (gn >= p.n) continue;
+              store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
+            }
           }
         }
-        continue;
       }
-      // Epilogue: D = C + acc, masked stores.  (The empty asm makes the row
-      // index opaque, so the row addresses are computed here instead of being
-      // hoisted above the K loop, where registers are scarce.)
-      int row0 = wrow0 + r16;
-      asm volatile("" : "+v"(row0));
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int gm = row0 + i * 16;
-        bool row_ok = gm < row_end;
-        if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
-        if (!row_ok) continue;
-        const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
-        const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int gn = n0 + wn * TN + j * 16 + 4 * q4;
-          if (gn >= p.n) continue;
-          store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
-        }
-      }
+      asm volatile("" ::: "memory");  // every store precedes the next unit's first wait
     }
+    u = nx;
+    pre = pre_next;
   }
 }
 
