@@ -49,6 +49,7 @@ def kernel_family(case_label: str) -> str:
     return "gemm"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_CAL_MB = 256  # plain device-to-device copy used to calibrate FETCH_SIZE / WRITE_SIZE
+TIMED_MARK = "timed: "  # roctx range name prefix of the timed launches of the dominant case
 
 
 def kernel_source_hash(family: str) -> str:
@@ -114,6 +115,21 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
     for r in stats:
         lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    timed = [r for r in stats if r["Name"].startswith(TIMED_MARK)]
+    if timed:
+        r = timed[0]
+        lines += ["", "## Timed launches of the dominant case", "",
+                  f"- rocprofv3 (launches inside the `{r['Name'][:80]}` roctx range, renamed by "
+                  f"`--kernel-rename`): {r['Calls']} calls, average {float(r['AverageNs']) / 1e3:.1f} us"]
+        try:
+            with open(os.path.join(prof_dir, "bench_line.json")) as f:
+                line = json.loads([t for t in f.read().splitlines() if t.startswith("{")][-1])
+            roof = line["roofline"]
+            lines.append(f"- the same run's bench line (HIP events on the launch stream): "
+                         f"{roof['avg_launch_us']:.1f} us per launch, {roof['achieved']:.1f} {roof['unit']}, "
+                         f"frac {roof['frac']:.3f}; value {line['value']:.1f} {line['unit']}")
+        except (OSError, ValueError, KeyError, IndexError):
+            lines.append("- bench line of the profiled run: not found")
     traffic = None
     lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", ""]
     if None not in (f_gemm, w_gemm, f_copy, w_copy):
@@ -142,6 +158,39 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+class _RangeMarks:
+    """roctx ranges around the timed launches of the dominant case, so that a
+    ``rocprofv3 --kernel-trace --kernel-rename`` run of this same command reports those
+    launches as their own row. Outside a profiler the calls are no-ops; without the
+    library the marks are skipped (they only label a trace)."""
+
+    def __init__(self):
+        import ctypes
+        self._lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
+            try:
+                lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        else:
+            return
+        lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        lib.roctxRangePushA.restype = ctypes.c_int
+        lib.roctxRangePop.argtypes = []
+        lib.roctxRangePop.restype = ctypes.c_int
+        self._lib = lib
+
+    def push(self, msg: str):
+        if self._lib is not None:
+            self._lib.roctxRangePushA(msg.encode())
+
+    def pop(self):
+        if self._lib is not None:
+            self._lib.roctxRangePop()
+
 
 
 def _cdiv(a, b):
@@ -427,13 +476,16 @@ def main():
             c.call()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    marks = _RangeMarks()
     t0 = time.perf_counter()
     for s in range(args.steps):
         for i, c in enumerate(cases):
             if i == dom:
+                marks.push(TIMED_MARK + c.label)
                 ev[s][0].record()
                 c.call()
                 ev[s][1].record()
+                marks.pop()
             else:
                 c.call()
     torch.cuda.synchronize()
