@@ -199,6 +199,12 @@ def test_masked_fp32_out():
     _check_masked(x, run_masked(x), "masked fp32")
 
 
+def test_masked_narrow_n():
+    """N <= 128 takes the 128x128 masked tiles (wider N takes the 256-row tiles)."""
+    x = gen_masked(4, 272, 128, 512, seed=37, masked_m=[272, 129, 0, 5])
+    _check_masked(x, run_masked(x, expected_m=64), "masked n=128")
+
+
 def test_num_cus_cap_gives_same_bits():
     x = gen_dense(640, 768, 1024, seed=36)
     ref_bits = raw_bits(run_dense(x))
