@@ -250,6 +250,15 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr int HOLD = 2, FIRST = NI - HOLD;
   constexpr int T = FM * FN, T1 = FIRST * NO, P2 = HOLD * NO;
   constexpr int RING = 4, LAG = 3;
+  // With two stages a slab's direct loads can start only once the previous
+  // slab in its stage has been read by every wave (the barrier), and half a
+  // slab's worth of loads queued at once stalls the issuing waves behind the
+  // vector-memory queue.  So the loads of slab s go out in two groups: the
+  // first P2L in the part 2 of slab s - 2, one per MFMA, the other P1L at the
+  // first MFMAs of slab s - 1 (its stage is free then, and the barrier that
+  // ends that part 1 waits for them).
+  constexpr int P1L = (STAGES == 2 && LOADS / 2 <= T1) ? LOADS / 2 : 0;
+  constexpr int P2L = LOADS - P1L;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
   static_assert(TN <= 128, "a wave's columns touch at most two 128-column scale blocks");
   static_assert(FIRST >= HOLD && NO >= 2, "two-part slab schedule");
@@ -495,9 +504,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       // reading slab `it` (its stage takes slab it + STAGES) and slab it + 1 has
       // landed; part 2 multiplies rows FIRST .. FM-1 (column-major) from
       // registers only, issuing one direct load of slab it + STAGES per MFMA
-      // and reading slab it + 1's B fragments, first A fragment and scales as
-      // the columns free up.  No LDS latency and no burst of loads sits at the
-      // barrier.  Each slab's FP32 promotion trails its MFMAs by LAG and
+      // (with two stages only the first P2L; the rest go out at the start of
+      // the next part 1) and reading slab it + 1's B fragments, first A
+      // fragment and scales as the columns free up.  No LDS latency and no
+      // burst of loads sits at the barrier.  Each slab's FP32 promotion trails its MFMAs by LAG and
       // carries across the slab boundary.
       // inner / outer fragment of the slab's MFMA t (part 1: inner-major over
       // the streamed fragments, part 2: outer-major over the held ones), and
@@ -599,6 +609,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             }
           };
 
+          // the last P1L loads of slab it + 1 (slab 1 went out whole before the
+          // loop, or with the previous unit's epilogue)
+          const bool late_loads = P1L > 0 && it > 0;
+          const SlabRsrc pr = slab_rsrc(sr, kb + 1, it + 1 < nkb);
           if (wave_live) {
 #pragma unroll
             for (int t = 0; t < T1; ++t) {
@@ -607,9 +621,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
               if (o == NO / 2 && n < HOLD) fh[n] = read_frag(Is + (FIRST + n) * 16 * 128, sw0, sw1);
               mma(t, fo[o], fi);
               promote(t - LAG);
+              if (t < P1L && late_loads) issue_load(sr, pr, nxt, P2L + t);
               if (o == NO - 1 && n + 1 < FIRST) fi = fi_next;
               if (o == NO - 1) __builtin_amdgcn_sched_barrier(0);
             }
+          } else if (late_loads) {
+#pragma unroll
+            for (int idx = P2L; idx < LOADS; ++idx) issue_load(sr, pr, nxt, idx);
           }
 
           // slab it + 1 has landed (this wave's part of it); right after a
@@ -631,7 +649,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
               const int w = t - T1, o = w / HOLD, h = w % HOLD;
               mma(t, fo[o], fh[h]);
               promote(t - LAG);
-              if (w < LOADS) issue_load(sr, nr, cur, w);
+              if (w < P2L) issue_load(sr, nr, cur, w);
               if (h == HOLD - 1) {
                 fo[o] = read_frag(On + o * 16 * 128, sw0, sw1);
                 if (o == 0) fi = read_frag(In, sw0, sw1);
@@ -647,10 +665,10 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             }
           } else {
 #pragma unroll
-            for (int idx = 0; idx < (LOADS < P2 ? LOADS : P2); ++idx) issue_load(sr, nr, cur, idx);
+            for (int idx = 0; idx < (P2L < P2 ? P2L : P2); ++idx) issue_load(sr, nr, cur, idx);
           }
 #pragma unroll
-          for (int idx = P2; idx < LOADS; ++idx) issue_load(sr, nr, cur, idx);
+          for (int idx = P2; idx < P2L; ++idx) issue_load(sr, nr, cur, idx);
         }
         // promote the last slab's tail
         if (wave_live) {
