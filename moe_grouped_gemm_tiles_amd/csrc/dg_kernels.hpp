@@ -741,9 +741,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
 }
 
 // Split-K reduction: D = C + sum over splits (in split order) of the FP32
-// partials ws[s][m][n]; one thread per 4 consecutive columns of a row.
+// partials ws[s][m][n]; one thread per 4 consecutive columns of a row.  The
+// partials are loaded eight at a time before they are added (in order), so
+// their latencies overlap instead of adding up.
 template <bool BF16_OUT, bool HAS_C>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const Params p) {
+  constexpr int BATCH = 8;
   const int vec_per_row = (p.n + 3) >> 2;
   const int64_t total = (int64_t)p.m * vec_per_row;
   const int64_t split_stride = (int64_t)p.m * p.ldw;
@@ -752,7 +755,15 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const Params p) {
     const int gn = (int)(idx - (int64_t)gm * vec_per_row) * 4;
     const float* W = p.ws + (int64_t)gm * p.ldw + gn;
     f32x4 v = *reinterpret_cast<const f32x4*>(W);
-    for (int s = 1; s < p.splits; ++s) v += *reinterpret_cast<const f32x4*>(W + s * split_stride);
+    for (int s = 1; s < p.splits; s += BATCH) {
+      f32x4 t[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (s + j < p.splits) t[j] = *reinterpret_cast<const f32x4*>(W + (s + j) * split_stride);
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (s + j < p.splits) v += t[j];
+    }
     store_out<BF16_OUT, HAS_C>(p, (int64_t)gm * p.ldc, gn, (int64_t)gm * p.ldd, v);
   }
 }
