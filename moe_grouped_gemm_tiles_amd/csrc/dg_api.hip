@@ -33,6 +33,7 @@ int g_device_cus[kMaxDevices] = {0};
 std::once_flag g_env_once;
 bool g_print_configs = false;
 int g_force_splits = 0;
+bool g_tail_split = true;  // DG_TAIL_SPLIT=0 keeps the ragged last round of contiguous calls
 std::atomic<int> g_tile_n{0};  // forced width of the 256-row tiles (0 = automatic)
 
 void read_env() {
@@ -41,6 +42,8 @@ void read_env() {
     g_print_configs = s && std::atoi(s) != 0;
     const char* f = std::getenv("DG_FORCE_SPLITS");
     g_force_splits = f ? std::atoi(f) : 0;
+    const char* ts = std::getenv("DG_TAIL_SPLIT");
+    g_tail_split = !(ts && std::atoi(ts) == 0);
     const char* tn = std::getenv("DG_TILE_N");
     const int w = tn ? std::atoi(tn) : 0;
     if (w == 256 || w == 224 || w == 160) g_tile_n.store(w);
@@ -393,6 +396,34 @@ dg_status contiguous_impl(const void* a, const void* sfa, int64_t ld_sfa, const 
   st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
   const Cfg cfg = n > 128 ? choose_wide(cdiv(m_total, 256), n, cus) : kCfg128;
+  // Ragged last round: the token count sets the number of 256-row tiles, so
+  // the last round of a persistent launch can keep only a few CUs busy for a
+  // whole tile time.  When it would be at most half full, the rows of that
+  // round go to a second launch of 128x128 tiles (four per 256-row tile, two
+  // workgroups per CU) that fits in one round.  Rows are split at a multiple
+  // of 256, so every 128-row block keeps its group; the per-element sums are
+  // the same, so the bits do not change.
+  const int64_t col_tiles = cdiv(n, cfg.bn);
+  const int64_t slots = static_cast<int64_t>(cus) * cfg.per_cu;
+  const int64_t tiles = static_cast<int64_t>(cdiv(m_total, 256)) * col_tiles;
+  const int64_t rounds = tiles / slots, rem = tiles % slots;
+  if (g_tail_split && cfg.bm == 256 && rounds >= 1 && rem > 0 && 2 * rem <= slots) {
+    const int main_rows = static_cast<int>(rounds * slots / col_tiles) * 256;
+    const int tail_rows = m_total - main_rows;
+    const int64_t tail_tiles = static_cast<int64_t>(cdiv(tail_rows, 128)) * cdiv(n, 128);
+    if (main_rows > 0 && tail_rows > 0 && tail_tiles <= static_cast<int64_t>(cus) * kCfg128.per_cu) {
+      dg::Params q = p;
+      p.m = main_rows;
+      st = launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, e8m0, 1, stream);
+      if (st != DG_SUCCESS) return st;
+      q.a += static_cast<int64_t>(main_rows) * k;
+      q.sfa += main_rows;
+      q.d = static_cast<uint8_t*>(d) + static_cast<int64_t>(main_rows) * n * dtype_size(d_dtype);
+      q.grp += main_rows;
+      q.m = tail_rows;
+      return launch<dg::MODE_CONTIG>(q, kCfg128, d_dtype, false, e8m0, 1, stream);
+    }
+  }
   return launch<dg::MODE_CONTIG>(p, cfg, d_dtype, false, e8m0, 1, stream);
 }
 

@@ -67,7 +67,9 @@ def test_contiguous_moe_full_size():
     rng = np.random.default_rng(22)
     starts = np.concatenate([[0], np.cumsum([-(-int(s) // 128) * 128 for s in x["m_sizes"]])[:-1]])
     ends = starts + x["m_sizes"] - 1
-    rows = _sample(rng, x["m_total"], 64, must=np.concatenate([starts, ends]))
+    # rows of the last 512, which a ragged last round sends to the 128x128 launch
+    tail = x["m_total"] - np.array([512, 511, 384, 257, 256, 129, 1])
+    rows = _sample(rng, x["m_total"], 64, must=np.concatenate([starts, ends, tail]))
     rows = rows[written[rows]]
     cols = _sample(rng, 4096, 512, must=(0, 4095))
     ref, w = oracle.ref_contiguous(x["a"], x["sfa"], x["b"], x["sfb"], mi, rows=rows, cols=cols)

@@ -215,6 +215,27 @@ def test_num_cus_cap_gives_same_bits():
         dg.set_num_cus(0)
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_contiguous_ragged_last_round_split(fmt):
+    """Capped at 4 CUs, 1280 rows (5 row tiles of 256) x 2 column tiles leave a
+    last round of 2 tiles in 4 slots, so rows 1024.. go to a second launch of
+    128x128 tiles; the split cuts through group 1.  The bits must equal the
+    uncapped call (one round, one launch) and the oracle."""
+    x = gen_contiguous(3, 512, 512, seed=38, m_sizes=[300, 700, 100], scale_fmt=fmt)
+    assert x["m_total"] == 1280
+    whole = run_contiguous(x)
+    try:
+        dg.set_num_cus(4)
+        split = run_contiguous(x)
+    finally:
+        dg.set_num_cus(0)
+    assert np.array_equal(raw_bits(split), raw_bits(whole))
+    ref_fn = oracle.ref_contiguous if fmt == "fp32" else oracle.ref_contiguous_ue8m0
+    ref, written = ref_fn(x["a"], x["sfa"], x["b"], x["sfb"], x["m_indices"])
+    oracle.assert_close(as_f64(split)[written], ref[written], f"contiguous tail split {fmt}")
+    assert (raw_bits(split)[~written] == sentinel_of(split)).all()
+
+
 @pytest.mark.parametrize("m,out", [(48, "fp32"), (128, "bf16"), (100, "fp32")])
 def test_dense_split_k_with_c(m, out):
     """Skinny M takes the split-K path (FP32 partials + ordered reduction); C is added once."""
