@@ -74,6 +74,55 @@ def lookup_traffic(case_label: str):
     return ent.get("traffic_bytes")
 
 
+def counter_summary(prof_dir: str, out_md: str, case_label: str, command: str, kernel: str, flops: float,
+                    launch_us: float, cus: int = 256, xcds: int = 8):
+    """Summarise rocprofv3 --pmc runs (every */*counter_collection.csv under prof_dir) for one kernel:
+    the mean of each counter per dispatch, and, where the counters are there, the ratios they give."""
+    import csv
+    import glob
+
+    per, dur, ratio = {}, {}, []
+    for f in glob.glob(os.path.join(prof_dir, "**", "*counter_collection.csv"), recursive=True):
+        rows = [r for r in csv.DictReader(open(f)) if kernel in r["Kernel_Name"]]
+        for r in rows:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur[(f, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                ratio.append(float(r["Counter_Value"]) / dur[(f, r["Dispatch_Id"])])
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    mean_dur = sum(dur.values()) / len(dur) if dur else 0.0
+    lines = [f"# rocprofv3 counters: {case_label}", "", "Command (run from the repository root):", "", "```",
+             command, "```", "", f"Kernel: `{kernel}`; mean per dispatch over the dispatches of the run.", "",
+             "| counter | dispatches | mean per dispatch |", "|---|---:|---:|"]
+    for k in sorted(mean):
+        lines.append(f"| {k} | {len(per[k])} | {mean[k]:.4g} |")
+    lines += ["", "## Derived", ""]
+    mfma = flops / (2 * 16 * 16 * 128)  # v_mfma_f32_16x16x128_f8f6f4 instructions of the algorithmic work
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        lines.append(f"- MFMA instructions of the algorithmic work: {mfma:.4g}; SQ_VALU_MFMA_BUSY_CYCLES per "
+                     f"instruction: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.2f}")
+    lines.append(f"- dispatch duration under the counter runs: {mean_dur * 1e6:.1f} us "
+                 f"(the same launch unprofiled, from the bench line: {launch_us:.1f} us)")
+    if ratio and mean_dur < 100e-6:
+        lines.append("- GRBM_GUI_ACTIVE over dispatches this short does not give the clock (the counter window "
+                     "is wider than the dispatch timestamps); no clock or busy fraction derived")
+        ratio = []
+        mean.pop("GRBM_GUI_ACTIVE")
+    if ratio:
+        lines.append(f"- GRBM_GUI_ACTIVE (summed over the {xcds} XCDs) / {xcds} / dispatch duration: "
+                     f"{sum(ratio) / len(ratio) / xcds / 1e9:.2f} GHz (the clock the kernel ran at)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] / xcds * 4 * cus)
+            lines.append(f"- SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {4 * cus} SIMDs): {busy:.3f} "
+                         f"(the matrix cores were busy that fraction of the kernel's cycles)")
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean and mean["SQ_LDS_IDX_ACTIVE"] > 0:
+        lines.append(f"- SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: "
+                     f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.4f}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, kernel: str = "gemm_kernel"):
     """Summarise rocprofv3 output (trace/, fetch/, write/ under prof_dir) into a short text file and
     record the calibrated HBM traffic of the GEMM kernel in profiles/traffic.json."""
@@ -414,10 +463,16 @@ def main():
                     help="summarise rocprofv3 output collected for CASE_LABEL and exit (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command line recorded in the profile summary")
     ap.add_argument("--profile-kernel", default="gemm_kernel", help="name substring of the profiled kernel")
+    ap.add_argument("--counter-summary", nargs=5, metavar=("PROF_DIR", "OUT_MD", "CASE_LABEL", "FLOPS", "LAUNCH_US"),
+                    help="summarise rocprofv3 --pmc counter runs for CASE_LABEL and exit (no GPU needed)")
     args = ap.parse_args()
 
     if args.profile_summary:
         profile_summary(*args.profile_summary, command=args.profile_command, kernel=args.profile_kernel)
+        return
+    if args.counter_summary:
+        d, out, label, flops, us = args.counter_summary
+        counter_summary(d, out, label, args.profile_command, args.profile_kernel, float(flops), float(us))
         return
 
     if args.gpus != 1:
