@@ -165,6 +165,7 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
         lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     timed = [r for r in stats if r["Name"].startswith(TIMED_MARK)]
+    per_call = 1  # kernel dispatches per library call (a contiguous call with a split tail makes two)
     if timed:
         r = timed[0]
         lines += ["", "## Timed launches of the dominant case", "",
@@ -174,6 +175,10 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
             with open(os.path.join(prof_dir, "bench_line.json")) as f:
                 line = json.loads([t for t in f.read().splitlines() if t.startswith("{")][-1])
             roof = line["roofline"]
+            per_call = max(1, round(int(timed[0]["Calls"]) / int(line["steps"])))
+            if per_call > 1:
+                lines.append(f"- {per_call} dispatches per call ({line['steps']} timed calls): "
+                             f"{per_call * float(timed[0]['AverageNs']) / 1e3:.1f} us per call")
             lines.append(f"- the same run's bench line (HIP events on the launch stream): "
                          f"{roof['avg_launch_us']:.1f} us per launch, {roof['achieved']:.1f} {roof['unit']}, "
                          f"frac {roof['frac']:.3f}; value {line['value']:.1f} {line['unit']}")
@@ -184,11 +189,12 @@ def profile_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
     if None not in (f_gemm, w_gemm, f_copy, w_copy):
         kf = f_copy * 1024 / cal_bytes
         kw = w_copy * 1024 / cal_bytes
-        traffic = f_gemm * 1024 / kf + w_gemm * 1024 / kw
+        traffic = (f_gemm * 1024 / kf + w_gemm * 1024 / kw) * per_call
         lines += [f"- copy calibration ({COPY_CAL_MB} MiB device copy): FETCH_SIZE {f_copy:.0f} KiB "
                   f"(factor {kf:.3f}), WRITE_SIZE {w_copy:.0f} KiB (factor {kw:.3f})",
                   f"- `{kernel}`: FETCH_SIZE {f_gemm:.0f} KiB, WRITE_SIZE {w_gemm:.0f} KiB per dispatch",
-                  f"- calibrated HBM traffic per launch: {traffic / 1e6:.1f} MB"]
+                  f"- calibrated HBM traffic per launch: {traffic / 1e6:.1f} MB"
+                  + (f" ({per_call} dispatches of the mean above)" if per_call > 1 else "")]
         rec = {}
         try:
             rec = json.load(open(TRAFFIC_FILE))
