@@ -99,8 +99,9 @@ def counter_summary(prof_dir: str, out_md: str, case_label: str, command: str, k
     lines += ["", "## Derived", ""]
     mfma = flops / (2 * 16 * 16 * 128)  # v_mfma_f32_16x16x128_f8f6f4 instructions of the algorithmic work
     if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-        lines.append(f"- MFMA instructions of the algorithmic work: {mfma:.4g}; SQ_VALU_MFMA_BUSY_CYCLES per "
-                     f"instruction: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.2f}")
+        lines.append(f"- 16x16x128 FP8 MFMAs of the algorithmic work: {mfma:.4g}; SQ_VALU_MFMA_BUSY_CYCLES per "
+                     f"algorithmic MFMA: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.2f} (32 when the kernel "
+                     f"multiplies no padding, masked or tile-rounding rows)")
     lines.append(f"- dispatch duration under the counter runs: {mean_dur * 1e6:.1f} us "
                  f"(the same launch unprofiled, from the bench line: {launch_us:.1f} us)")
     if ratio and mean_dur < 100e-6:
