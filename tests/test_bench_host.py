@@ -47,3 +47,62 @@ def test_bench_refuses_more_than_one_gpu():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT)
     assert p.returncode != 0 and "one GPU" in p.stderr
+
+
+def _csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=header)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_profile_summary_counts_dispatches_per_call(tmp_path, monkeypatch):
+    """A call made of two dispatches (main launch + ragged-tail launch): the renamed
+    trace row holds 2 dispatches per timed call, and the copy-calibrated traffic of
+    one call is twice the per-dispatch mean."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    d = tmp_path / "prof"
+    stats_h = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"]
+    _csv(str(d / "trace" / "t_kernel_stats.csv"), stats_h,
+         [dict(Name="timed: contiguous X", Calls=10, AverageNs=400000, MinNs=1, MaxNs=2)])
+    ctr_h = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value"]
+    for sub, name, gemm_vals, copy_val in (("fetch", "FETCH_SIZE", [1000.0, 3000.0], 131072.0),
+                                           ("write", "WRITE_SIZE", [500.0, 500.0], 262144.0)):
+        rows = [dict(Kernel_Name="__amd_rocclr_copyBuffer", Dispatch_Id=1, Counter_Name=name, Counter_Value=copy_val)]
+        rows += [dict(Kernel_Name="void dg::gemm_kernel<256>", Dispatch_Id=2 + i, Counter_Name=name, Counter_Value=v)
+                 for i, v in enumerate(gemm_vals)]
+        _csv(str(d / sub / "x_counter_collection.csv"), ctr_h, rows)
+    line = dict(steps=5, value=1.0, unit="TFLOPS",
+                roofline=dict(avg_launch_us=800.0, achieved=1.0, unit="TFLOP/s", frac=0.1))
+    (d / "bench_line.json").write_text(json.dumps(line) + "\n")
+    out = tmp_path / "s.md"
+    bench.profile_summary(str(d), str(out), "contiguous X", "cmd")
+    text = out.read_text()
+    assert "2 dispatches per call (5 timed calls): 800.0 us per call" in text
+    rec = json.loads((tmp_path / "traffic.json").read_text())["cases"]["contiguous X"]
+    # factors: 131072 KiB / 256 MiB = 0.5 (fetch), 262144 KiB / 256 MiB = 1.0 (write)
+    assert abs(rec["traffic_bytes"] - 2 * (2000 * 1024 / 0.5 + 500 * 1024 / 1.0)) < 1e-6
+
+
+def test_counter_summary_derives_clock_and_busy(tmp_path):
+    """GRBM_GUI_ACTIVE is summed over 8 XCDs: 8 x 1.9e9 x 200 us over a 200 us dispatch is
+    1.9 GHz; busy cycles equal to half of 1024 SIMDs x those cycles is 0.5 busy."""
+    d = tmp_path / "ctr"
+    cyc = 1.9e9 * 200e-6
+    busy = 0.5 * cyc * 1024
+    flops = busy / 32 * (2 * 16 * 16 * 128)
+    h = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = [dict(Kernel_Name="gemm_kernel<256, 256", Dispatch_Id=1, Counter_Name="GRBM_GUI_ACTIVE",
+                 Counter_Value=8 * cyc, Start_Timestamp=1000, End_Timestamp=201000),
+            dict(Kernel_Name="gemm_kernel<256, 256", Dispatch_Id=1, Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES",
+                 Counter_Value=busy, Start_Timestamp=1000, End_Timestamp=201000)]
+    _csv(str(d / "p1" / "p_counter_collection.csv"), h, rows)
+    out = tmp_path / "c.md"
+    bench.counter_summary(str(d), str(out), "case", "cmd", "gemm_kernel<256, 256", flops, 190.0)
+    text = out.read_text()
+    assert "SQ_VALU_MFMA_BUSY_CYCLES per algorithmic MFMA: 32.00" in text
+    assert "dispatch duration: 1.90 GHz" in text
+    assert "SIMDs): 0.500" in text
