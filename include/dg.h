@@ -107,6 +107,9 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
  *            groups breaks the layout contract (rows of other groups are
  *            left unwritten, never out of bounds).
  * m_total % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ * The call enqueues one kernel, or two on the same stream when the last round
+ * of 256-row tiles would keep at most half the CUs busy (its rows then go to
+ * 128x128 tiles; same bits).  DG_TAIL_SPLIT=0 in the environment keeps one.
  */
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa,
                                               const void* b, const float* sfb,
