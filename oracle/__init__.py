@@ -18,6 +18,8 @@ What it computes, written out plainly in FP64 with numpy:
 * the FP8 quantization a caller performs before the GEMM, per-token 1x128
   and per-block 128x128, FP32 or UE8M0 scales (``quant.py``);
 * the weighted-ReLU MQA logits of the indexer (``mqa.py``);
+* the scale-factor layout transform: per-row scales to the transposed,
+  aligned FP32 form or the packed UE8M0 form (``layout.py``);
 * the acceptance check (``check.py``).
 
 Sources, by page title and section:
@@ -63,4 +65,5 @@ from .ue8m0 import (  # noqa: F401
 from .kgrouped import k_offsets, ref_k_grouped  # noqa: F401
 from .quant import e4m3_encode_rne, quant_per_token, quant_per_block  # noqa: F401
 from .mqa import ref_mqa_logits  # noqa: F401
+from .layout import transform_sf  # noqa: F401
 from .check import tolerance_report, assert_close, TOL_REL, TOL_RMS, TOL_COS  # noqa: F401
