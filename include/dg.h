@@ -272,6 +272,32 @@ dg_status dg_fp8_mqa_logits(const void* q, const void* kv, const float* kv_sf, c
                             int s, int s_kv, int num_heads, int head_dim, int clean_logits,
                             hipStream_t stream);
 
+/*
+ * Scale-factor layout transform.
+ *   [README] "Utilities": transform_sf_into_required_layout,
+ *   get_mn_major_tma_aligned_tensor and
+ *   get_mn_major_tma_aligned_packed_ue8m0_tensor; "Interfaces > Notices": the
+ *   LHS scale factor is transposed and aligned, and the UE8M0 form packs four
+ *   scale bytes into one int.
+ *
+ * sf      DEVICE FP32 [num_groups][mn][kb] row-major per-row scales (one per
+ *         row and 128-wide K block), 4-B aligned.
+ * out     DEVICE, 16-B aligned, caller-allocated:
+ *           ue8m0 == 0: FP32 [num_groups][kb][ld_out], out[g][k][r] = sf[g][r][k];
+ *           ue8m0 != 0: int32 [num_groups][ceil(kb/4)][ld_out]; byte j (least
+ *             significant first) of out[g][q][r] is the biased exponent field
+ *             (bits 30..23) of sf[g][r][4q+j] -- exactly the UE8M0 code when
+ *             the scale is a power of two -- and 127 where 4q+j >= kb.
+ *         Columns mn..ld_out-1 are not written.
+ * ld_out  >= mn and a multiple of 4 (dg_get_sf_aligned_size(mn)), else
+ *         DG_ERROR_INVALID_VALUE.  The result is the sfa operand of the GEMM
+ *         entry points (masked: one group per expert).
+ * num_groups, mn or kb == 0 -> DG_SUCCESS with nothing enqueued; more than
+ * 65535 groups -> DG_ERROR_NOT_SUPPORTED.
+ */
+dg_status dg_transform_sf_into_required_layout(const float* sf, void* out, int num_groups, int mn, int kb,
+                                               int64_t ld_out, int ue8m0, hipStream_t stream);
+
 /* Row (M-grouped) and K (K-grouped) alignment of group segments in the
  * contiguous layouts (128).
  * [README] "Utilities": get_mk_alignment_for_contiguous_layout. */

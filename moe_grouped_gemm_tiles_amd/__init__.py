@@ -52,6 +52,9 @@ __all__ = [
     "per_token_cast_to_fp8",
     "per_block_cast_to_fp8",
     "fp8_mqa_logits",
+    "transform_sf_into_required_layout",
+    "get_mn_major_tma_aligned_tensor",
+    "get_mn_major_tma_aligned_packed_ue8m0_tensor",
     "get_mk_alignment_for_contiguous_layout",
     "get_sf_aligned_size",
     "set_num_cus",
@@ -93,6 +96,7 @@ _SIGNATURES = {
     "dg_per_token_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp]),
     "dg_per_block_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _vp]),
     "dg_fp8_mqa_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "dg_transform_sf_into_required_layout": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
@@ -428,6 +432,33 @@ def fp8_mqa_logits(q: torch.Tensor, kv_pair, weights: torch.Tensor, ks: torch.Te
                                _stream(out))
     _check(st)
     return out
+
+
+def transform_sf_into_required_layout(sf: torch.Tensor, ue8m0: bool = False) -> torch.Tensor:
+    """Per-row scales FP32 [mn, kb] (or [G, mn, kb]) -> the GEMM's sfa layout: FP32 [kb, ld]
+    (or [G, kb, ld]) transposed with ld = get_sf_aligned_size(mn), or with ``ue8m0`` the packed
+    int32 words [ceil(kb/4), ld] holding each scale's exponent byte (powers of two)."""
+    lib = load_library()
+    if sf.dtype != torch.float32 or not sf.is_cuda or sf.dim() not in (2, 3):
+        raise TypeError("sf must be a float32 GPU tensor [mn, kb] or [G, mn, kb]")
+    x = sf.contiguous()
+    g, mn, kb = (1, *x.shape) if x.dim() == 2 else x.shape
+    ld = int(lib.dg_get_sf_aligned_size(mn))
+    rows = (kb + 3) // 4 if ue8m0 else kb
+    out = torch.empty((g, rows, ld), dtype=torch.int32 if ue8m0 else torch.float32, device=x.device)
+    _check(lib.dg_transform_sf_into_required_layout(x.data_ptr(), out.data_ptr(), g, mn, kb, ld,
+                                                    1 if ue8m0 else 0, _stream(out)))
+    return out[0] if sf.dim() == 2 else out
+
+
+def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
+    """Transposed, 16-byte aligned FP32 scales (the README's name for the FP32 form)."""
+    return transform_sf_into_required_layout(sf, ue8m0=False)
+
+
+def get_mn_major_tma_aligned_packed_ue8m0_tensor(sf: torch.Tensor) -> torch.Tensor:
+    """Transposed, aligned scales packed into UE8M0 words (scales must be powers of two)."""
+    return transform_sf_into_required_layout(sf, ue8m0=True)
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libdg.so")
 RES = os.path.join(PKG, "libdg.resources.txt")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, f) for f in ("dg_api.hip", "dg_quant.hip", "dg_mqa.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("dg_api.hip", "dg_quant.hip", "dg_mqa.hip", "dg_layout.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("dg_kernels.hpp", "dg_common.hpp")] + [os.path.join(INCLUDE, "dg.h")]
 
 
