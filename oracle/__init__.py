@@ -60,6 +60,7 @@ from .ue8m0 import (  # noqa: F401
     decode_ue8m0_sf,
     ref_dense_ue8m0,
     ref_contiguous_ue8m0,
+    ref_k_grouped_ue8m0,
     ref_masked_ue8m0,
 )
 from .kgrouped import k_offsets, ref_k_grouped  # noqa: F401

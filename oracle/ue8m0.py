@@ -83,3 +83,13 @@ def ref_masked_ue8m0(a, sfa_words, b, sfb_words, masked_m, groups=None, cols=Non
     kb = a.shape[2] // BLOCK
     return ref_masked(a, decode_ue8m0_sf(sfa_words, kb, 1), b, decode_ue8m0_sf(sfb_words, kb, 2),
                       masked_m, groups, cols)
+
+
+def ref_k_grouped_ue8m0(a, sfa_words, b, sfb_words, ks, c=None, groups=None, rows=None, cols=None):
+    """K-grouped reference with packed UE8M0 scales, words along the global K blocks
+    (sfa_words [ceil(KB/4), ld], sfb_words [NB, ceil(KB/4)])."""
+    from .kgrouped import ref_k_grouped
+
+    kb = a.shape[1] // BLOCK
+    return ref_k_grouped(a, decode_ue8m0_sf(sfa_words, kb, 0), b, decode_ue8m0_sf(sfb_words, kb, 1), ks, c,
+                         groups, rows, cols)

@@ -348,3 +348,28 @@ def test_mqa_relu_placement_weights_linearity_and_untouched_marking():
     assert np.allclose((base - neg)[fin], want_lin[fin], rtol=1e-12, atol=1e-12)
     # a planted "no ReLU" oracle would give base + neg == 0 instead
     assert not np.allclose((want_lin + (-want_lin))[fin], want_abs[fin])
+
+
+def test_k_grouped_ue8m0_equals_fp32_form_of_the_same_powers_of_two():
+    """Packed UE8M0 words along the global K blocks (a word may hold blocks of two
+    groups: ks = 128 + 384 + 0 + 256 puts group boundaries inside words) decode to
+    the same K-grouped GEMM as the FP32 scales they were packed from."""
+    from workloads.gen import _draw, pack_ue8m0, quantize_per_block, quantize_per_row_block, sf_to_mn_major
+
+    rng = np.random.default_rng(71)
+    m, n = 9, 200
+    ks = np.array([128, 384, 0, 256], np.int32)
+    k = int(ks.sum())
+    a, a_s = quantize_per_row_block(_draw(rng, (m, k)), True)
+    b, b_s = quantize_per_block(_draw(rng, (n, k)), True)
+    c = _draw(rng, (4, m, n))
+    sfa = sf_to_mn_major(a_s)
+    fp32 = oracle.ref_k_grouped(a, sfa, b, b_s, ks, c)
+    words_a = pack_ue8m0(np.where(np.arange(sfa.shape[1]) < m, sfa, 1.0), axis=0)
+    ue = oracle.ref_k_grouped_ue8m0(a, words_a, b, pack_ue8m0(b_s, axis=1), ks, c)
+    assert np.array_equal(fp32, ue)
+    # and a scale moved to the neighbouring byte (a per-group word restart) would not
+    bad = words_a.copy().view(np.uint32)
+    bad[0] = ((bad[0] << 8) | 127) & 0xFFFFFFFF
+    assert not np.array_equal(oracle.ref_k_grouped_ue8m0(a, bad.view(np.int32), b, pack_ue8m0(b_s, axis=1), ks, c),
+                              fp32)

@@ -243,14 +243,17 @@ def gen_masked(num_groups: int, m_max: int, n: int, k: int, seed: int, masked_m=
 
 
 def gen_k_grouped(num_groups: int, m: int, n: int, seed: int, ks=None, k_low: int = 1,
-                  k_high: int = 8192, with_c: bool = True):
+                  k_high: int = 8192, with_c: bool = True, scale_fmt: str = "fp32"):
     """K-grouped weight-gradient inputs: groups split K (tokens of each expert).
 
     Group token counts are drawn uniform in [k_low, k_high] unless ``ks`` is
     given, then padded up to multiples of 128 (the contiguous-layout
     alignment); draw order: counts, A, B, C.  A [M, K_total] is quantized per
     (row, 128-K block), B [N, K_total] per 128x128 block, C FP32 [G, M, N].
+    With ``scale_fmt='ue8m0'`` the scales are powers of two packed as UE8M0
+    words along the global K blocks (as for the dense GEMM).
     """
+    ue = scale_fmt == "ue8m0"
     rng = np.random.default_rng(seed)
     if ks is None:
         ks = rng.integers(k_low, k_high + 1, num_groups)
@@ -258,11 +261,15 @@ def gen_k_grouped(num_groups: int, m: int, n: int, seed: int, ks=None, k_low: in
     ks = np.asarray(ks, dtype=np.int32)
     assert ks.shape == (num_groups,) and (ks % SF_BLOCK == 0).all() and (ks >= 0).all()
     k_total = int(ks.sum())
-    a_codes, a_s = quantize_per_row_block(_draw(rng, (m, k_total)))
-    b_codes, b_s = _quantize_b(rng, n, k_total)
+    a_codes, a_s = quantize_per_row_block(_draw(rng, (m, k_total)), ue)
+    b_codes, b_s = _quantize_b(rng, n, k_total, ue)
     c = _draw(rng, (num_groups, m, n)) if with_c else None
-    return dict(kind="k_grouped", num_groups=num_groups, m=m, n=n, k=k_total, ks=ks,
-                a=a_codes, sfa=sf_to_mn_major(a_s), b=b_codes, sfb=b_s, c=c)
+    sfa = sf_to_mn_major(a_s)
+    if ue:
+        sfa = pack_ue8m0(np.where(np.arange(sfa.shape[1]) < m, sfa, 1.0), axis=0)
+        b_s = pack_ue8m0(b_s, axis=1)
+    return dict(kind="k_grouped", num_groups=num_groups, m=m, n=n, k=k_total, ks=ks, scale_fmt=scale_fmt,
+                a=a_codes, sfa=sfa, b=b_codes, sfb=b_s, c=c)
 
 
 def gen_quant_input(rows: int, k: int, seed: int, dtype: str = "bf16"):
