@@ -423,7 +423,8 @@ def cpu_baseline(inputs, budget_rows=4096, budget_cols=24576, quant_rows=8192):
             ue = x.get("scale_fmt") == "ue8m0"
             if kind == "k_grouped":
                 rows = np.arange(min(x["m"], budget_rows))
-                oracle.ref_k_grouped(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], x.get("c"), rows=rows, cols=cols)
+                ref = oracle.ref_k_grouped_ue8m0 if ue else oracle.ref_k_grouped
+                ref(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], x.get("c"), rows=rows, cols=cols)
                 nrows = len(rows)
             elif kind == "dense":
                 rows = np.arange(min(x["m"], budget_rows))

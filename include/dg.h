@@ -219,6 +219,25 @@ dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_
                                          int num_groups, int m, int n, int k_total, hipStream_t stream);
 
 /*
+ * The two K-grouped GEMMs above with packed UE8M0 scale factors.
+ *   [README] "Utilities": a K-grouped GEMM packing kernel for MN-major
+ *   UE8M0 scales; "Interfaces > Notices": UE8M0 scales packed four per int.
+ * sfa  int32 words [ceil(k_total/512)][ld_sfa]: byte j (least significant
+ *      first) of word q scales A's global K block 4q + j (2^(byte-127)).
+ * sfb  int32 words [ceil(n/128)][ceil(k_total/512)], same packing along K.
+ * Words are packed along the global K blocks, so a word may hold blocks of
+ * two adjacent groups (group ranges are multiples of 128, not of 512).
+ * Everything else as for the FP32-scale forms.
+ */
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
+                                                    const void* b, const int32_t* sfb, const float* c, float* d,
+                                                    const int32_t* ks, int num_groups, int m, int n, int k_total,
+                                                    hipStream_t stream);
+dg_status dg_k_grouped_wgrad_fp8_gemm_nt_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa, const void* b,
+                                               const int32_t* sfb, float* d, const int32_t* ks, int num_groups,
+                                               int m, int n, int k_total, hipStream_t stream);
+
+/*
  * FP8 quantization of GEMM operands (the cast the GEMM's caller performs,
  * [README] "Interfaces > Notices": FP8 casting and transposition are the
  * caller's job, and the LHS scale factors must be transposed and aligned;

@@ -93,6 +93,10 @@ _SIGNATURES = {
                                                    _i32, _i32, _i32, _i32, _vp]),
     "dg_wgrad_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "dg_k_grouped_wgrad_fp8_gemm_nt": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                                                         _i32, _i32, _i32, _i32, _vp]),
+    "dg_k_grouped_wgrad_fp8_gemm_nt_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                    _vp]),
     "dg_per_token_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp]),
     "dg_per_block_cast_to_fp8": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _vp]),
     "dg_fp8_mqa_logits": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -298,8 +302,7 @@ def _k_grouped_args(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor):
         _dense_contig(t, nm)
     _fp8(a, "a")
     _fp8(b, "b")
-    _f32(sfa, "sfa")
-    _f32(sfb, "sfb")
+    ue = _sf(sfa, sfb)
     if d.dtype != torch.float32 or not d.is_cuda:
         raise TypeError("d must be a float32 GPU tensor")
     if ks.dtype != torch.int32 or not ks.is_cuda:
@@ -309,24 +312,26 @@ def _k_grouped_args(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor):
     g = ks.shape[0]
     if b.shape != (n, k) or d.shape != (g, m, n) or ks.dim() != 1:
         raise ValueError("shape mismatch")
-    if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
+    kr = _sf_rows(k, ue)
+    if sfa.dim() != 2 or sfa.shape[0] != kr or sfb.shape != ((n + 127) // 128, kr):
         raise ValueError("scale shape mismatch")
-    return a, sfa, b, sfb, g, m, n, k
+    return a, sfa, b, sfb, g, m, n, k, ue
 
 
 def k_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor,
                                      c: torch.Tensor | None = None):
-    """K-grouped GEMM: D[g] = C[g] + A[:, K_g] @ B[:, K_g].T (FP32), K_g given by ks (int32, device)."""
+    """K-grouped GEMM: D[g] = C[g] + A[:, K_g] @ B[:, K_g].T (FP32), K_g given by ks (int32, device);
+    FP32 scales or packed UE8M0 words (int32), by the scale tensors' dtype."""
     lib = load_library()
-    a, sfa, b, sfb, g, m, n, k = _k_grouped_args(a_pair, b_pair, d, ks)
+    a, sfa, b, sfb, g, m, n, k, ue = _k_grouped_args(a_pair, b_pair, d, ks)
     c_ptr = None
     if c is not None:
         if c.dtype != torch.float32 or c.shape != d.shape or not c.is_contiguous() or not c.is_cuda:
             raise ValueError("c must be a contiguous float32 GPU tensor shaped like d")
         c_ptr = c.data_ptr()
-    st = lib.dg_k_grouped_fp8_gemm_nt_contiguous(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
-                                                 sfb.data_ptr(), c_ptr, d.data_ptr(), ks.data_ptr(), g, m, n, k,
-                                                 _stream(d))
+    fn = lib.dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0 if ue else lib.dg_k_grouped_fp8_gemm_nt_contiguous
+    st = fn(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(), sfb.data_ptr(), c_ptr, d.data_ptr(),
+            ks.data_ptr(), g, m, n, k, _stream(d))
     _check(st)
     return d
 
@@ -358,9 +363,10 @@ def wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor):
 def k_grouped_wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, ks: torch.Tensor):
     """K-grouped weight gradient: D[g] += A[:, K_g] @ B[:, K_g].T in FP32."""
     lib = load_library()
-    a, sfa, b, sfb, g, m, n, k = _k_grouped_args(a_pair, b_pair, d, ks)
-    st = lib.dg_k_grouped_wgrad_fp8_gemm_nt(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
-                                            sfb.data_ptr(), d.data_ptr(), ks.data_ptr(), g, m, n, k, _stream(d))
+    a, sfa, b, sfb, g, m, n, k, ue = _k_grouped_args(a_pair, b_pair, d, ks)
+    fn = lib.dg_k_grouped_wgrad_fp8_gemm_nt_ue8m0 if ue else lib.dg_k_grouped_wgrad_fp8_gemm_nt
+    st = fn(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(), sfb.data_ptr(), d.data_ptr(),
+            ks.data_ptr(), g, m, n, k, _stream(d))
     _check(st)
     return d
 

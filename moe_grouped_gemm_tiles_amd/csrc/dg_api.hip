@@ -151,11 +151,7 @@ KernelFn pick_tile(const Cfg& c, const Epi& e) {
 
 template <int MODE>
 KernelFn pick_kernel(const Cfg& c, const Epi& e) {
-  if constexpr (MODE == dg::MODE_KGROUP) {
-    return pick_tile<MODE, false>(c, e);
-  } else {
-    return e.e8m0 ? pick_tile<MODE, true>(c, e) : pick_tile<MODE, false>(c, e);
-  }
+  return e.e8m0 ? pick_tile<MODE, true>(c, e) : pick_tile<MODE, false>(c, e);
 }
 
 const char* mode_name(int mode) {
@@ -470,9 +466,9 @@ dg_status masked_impl(const void* a, const void* sfa, int64_t ld_sfa, const void
   return launch<dg::MODE_MASKED>(p, cfg, d_dtype, false, e8m0, num_groups, stream);
 }
 
-dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const void* b, const float* sfb,
+dg_status k_grouped_impl(const void* a, const void* sfa, int64_t ld_sfa, const void* b, const void* sfb,
                          const float* c, float* d, const int32_t* ks, int num_groups, int m, int n, int k_total,
-                         hipStream_t stream) {
+                         bool e8m0, hipStream_t stream) {
   if (num_groups < 0) return DG_ERROR_INVALID_VALUE;
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, DG_DTYPE_FP32, m, n, k_total);
   if (st != DG_SUCCESS) return st;
@@ -483,9 +479,9 @@ dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const 
 
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
-  p.sfa = sfa;
+  p.sfa = static_cast<const float*>(sfa);
   p.b = static_cast<const uint8_t*>(b);
-  p.sfb = sfb;
+  p.sfb = static_cast<const float*>(sfb);
   p.c = c;
   p.d = d;
   p.grp = ks;
@@ -505,7 +501,7 @@ dg_status k_grouped_impl(const void* a, const float* sfa, int64_t ld_sfa, const 
   st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
   const Cfg cfg = (m > 128 && n > 128) ? choose_wide(static_cast<int64_t>(num_groups) * cdiv(m, 256), n, cus) : kCfg128;
-  return launch<dg::MODE_KGROUP>(p, cfg, DG_DTYPE_FP32, c != nullptr, false, num_groups, stream);
+  return launch<dg::MODE_KGROUP>(p, cfg, DG_DTYPE_FP32, c != nullptr, e8m0, num_groups, stream);
 }
 
 }  // namespace
@@ -568,7 +564,14 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, const int32_t* sf
 dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
                                               const float* sfb, const float* c, float* d, const int32_t* ks,
                                               int num_groups, int m, int n, int k_total, hipStream_t stream) {
-  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, c, d, ks, num_groups, m, n, k_total, stream);
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, c, d, ks, num_groups, m, n, k_total, false, stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
+                                                    const void* b, const int32_t* sfb, const float* c, float* d,
+                                                    const int32_t* ks, int num_groups, int m, int n, int k_total,
+                                                    hipStream_t stream) {
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, c, d, ks, num_groups, m, n, k_total, true, stream);
 }
 
 dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
@@ -580,7 +583,13 @@ dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int
 dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
                                          const float* sfb, float* d, const int32_t* ks, int num_groups, int m,
                                          int n, int k_total, hipStream_t stream) {
-  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, d, d, ks, num_groups, m, n, k_total, stream);
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, d, d, ks, num_groups, m, n, k_total, false, stream);
+}
+
+dg_status dg_k_grouped_wgrad_fp8_gemm_nt_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa, const void* b,
+                                               const int32_t* sfb, float* d, const int32_t* ks, int num_groups,
+                                               int m, int n, int k_total, hipStream_t stream) {
+  return k_grouped_impl(a, sfa, ld_sfa, b, sfb, d, d, ks, num_groups, m, n, k_total, true, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return kAlignM; }

@@ -189,6 +189,12 @@ def test_k_grouped_and_wgrad_validation(lib):
     assert w(P, 512, P, 128, P, 512, P, P, 256, 0, 256, 512, None) == 0
     kw = lib.dg_k_grouped_wgrad_fp8_gemm_nt
     assert kw(P, P, 256, P, P, P, None, 4, 256, 256, 1024, None) == INVALID  # no ks
+    ku = lib.dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0
+    assert ku(P, P, 256, P, P, None, P, P, 4, 256, 256, 1000, None) == UNSUPPORTED  # k % 128
+    assert ku(P, P, 100, P, P, None, P, P, 4, 256, 256, 1024, None) == INVALID      # ld_sfa < m
+    assert ku(P, P, 256, P, P, None, P, P, 0, 256, 256, 1024, None) == 0
+    kwu = lib.dg_k_grouped_wgrad_fp8_gemm_nt_ue8m0
+    assert kwu(P, P, 256, P, P, P, None, 4, 256, 256, 1024, None) == INVALID  # no ks
 
 
 def test_binding_leading_dimension_of_size_one_dims():

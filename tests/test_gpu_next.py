@@ -132,6 +132,29 @@ def test_k_grouped_wgrad_in_place_and_large_tiles():
     _check_kg(x, run_k_grouped(x, in_place=True), True, "k-grouped wgrad in place")
 
 
+def _check_kg_ue(x, d, with_c, what):
+    ref = oracle.ref_k_grouped_ue8m0(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], c=x["c"] if with_c else None)
+    got = as_f64(d)
+    for g in range(x["num_groups"]):
+        if x["ks"][g] == 0:
+            assert np.array_equal(got[g], ref[g]), f"{what}: empty group {g}"
+            continue
+        rep = oracle.assert_close(got[g], ref[g], f"{what} group {g}")
+        note(f"{what} group {g} (K={x['ks'][g]}): worst={rep['worst_ratio']:.3f} cos_dist={rep['cos_dist']:.2e}")
+
+
+@pytest.mark.parametrize("with_c", [True, False])
+def test_k_grouped_ue8m0_small(with_c):
+    # 128 + 0 + 384 + 256: group boundaries fall inside packed words
+    x = gen_k_grouped(4, 200, 300, seed=84, ks=[128, 0, 384, 256], scale_fmt="ue8m0")
+    _check_kg_ue(x, run_k_grouped(x, with_c=with_c), with_c, f"k-grouped ue8m0 c={with_c}")
+
+
+def test_k_grouped_ue8m0_wgrad_in_place_and_large_tiles():
+    x = gen_k_grouped(3, 384, 640, seed=85, ks=[1024, 128, 0], scale_fmt="ue8m0")
+    _check_kg_ue(x, run_k_grouped(x, in_place=True), True, "k-grouped ue8m0 wgrad in place")
+
+
 def test_k_grouped_single_group_equals_dense():
     x = gen_k_grouped(1, 256, 512, seed=82, ks=[1536], with_c=False)
     dk = as_f64(run_k_grouped(x, with_c=False))[0]

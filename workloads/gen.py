@@ -372,6 +372,9 @@ def workload(name: str):
         # weight gradient of the contiguous MoE layer: dW[g] [4096, 7168] over each expert's tokens
         return [dict(label="k-grouped wgrad G=8 M=4096 N=7168 K_g~U[1,8192]", kind="k_grouped", m=4096, n=7168,
                      num_groups=8, gen=lambda: gen_k_grouped(8, 4096, 7168, seed=5))]
+    if name == "k_grouped_wgrad_ue8m0":
+        return [dict(label="k-grouped wgrad ue8m0 G=8 M=4096 N=7168 K_g~U[1,8192]", kind="k_grouped", m=4096,
+                     n=7168, num_groups=8, gen=lambda: gen_k_grouped(8, 4096, 7168, seed=5, scale_fmt="ue8m0"))]
     if name == "quant_moe":
         # the casts feeding the contiguous MoE GEMM: token activations (1x128
         # scales, transposed) and the 8 experts' weights (128x128 scales), BF16 in
