@@ -61,6 +61,9 @@ __all__ = [
     "get_num_cus",
     "set_tile_n",
     "get_tile_n",
+    "set_num_sms",
+    "get_num_sms",
+    "get_tma_aligned_size",
     "library_path",
     "load_library",
 ]
@@ -490,3 +493,10 @@ def set_tile_n(w: int):
 
 def get_tile_n() -> int:
     return load_library().dg_get_tile_n()
+
+
+# The README's names for the same utilities ("Utilities": set_num_sms / get_num_sms cap the
+# compute units used; get_tma_aligned_size is the aligned leading dimension of the scales).
+set_num_sms = set_num_cus
+get_num_sms = get_num_cus
+get_tma_aligned_size = get_sf_aligned_size
