@@ -56,6 +56,21 @@ def _calls():
     args = ((fp8_dev(x["a"]), to_dev(x["sfa"])), (fp8_dev(x["b"]), to_dev(x["sfb"])), d, to_dev(x["ks"]),
             to_dev(x["c"]))
     out.append(("k-grouped", (lambda args=args: dg.k_grouped_fp8_gemm_nt_contiguous(*args)), d))
+    x = gen_k_grouped(3, 256, 384, seed=97, ks=[128, 384, 0], scale_fmt="ue8m0")
+    d = torch.empty(3, 256, 384, dtype=torch.float32, device="cuda:0")
+    args = ((fp8_dev(x["a"]), to_dev(x["sfa"])), (fp8_dev(x["b"]), to_dev(x["sfb"])), d, to_dev(x["ks"]),
+            to_dev(x["c"]))
+    out.append(("k-grouped ue8m0", (lambda args=args: dg.k_grouped_fp8_gemm_nt_contiguous(*args)), d))
+    sf = to_dev(np.exp2(np.random.default_rng(98).integers(-8, 8, (2, 70, 9))).astype(np.float32))
+    d = torch.empty(2, 3, 72, dtype=torch.int32, device="cuda:0")
+    lib = dg.load_library()
+
+    def layout(sf=sf, d=d):
+        st = lib.dg_transform_sf_into_required_layout(sf.data_ptr(), d.data_ptr(), 2, 70, 9, 72, 1,
+                                                      torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    out.append(("scale layout ue8m0", layout, d))
     return out
 
 
