@@ -46,7 +46,9 @@
  * that stream needs it, grown (after synchronising that stream) when a larger
  * shape needs more, kept until process exit.  Calls under graph capture must
  * therefore be preceded by one uncaptured call of the same shape on the
- * capture stream; a captured graph uses that stream's workspace.
+ * capture stream; a captured graph uses that stream's workspace.  Host
+ * threads may share a stream: the workspace stays locked from its lookup until
+ * the call's kernels are enqueued.
  */
 #ifndef DG_H
 #define DG_H

@@ -163,14 +163,17 @@ const char* mode_name(int mode) {
 // Kernels on one stream run in order, so one buffer per stream is race-free.
 // Growing it synchronises that stream before freeing the old buffer; this is
 // the only allocation the library makes and it happens outside the kernels.
+// The caller keeps `lock` held until its kernels that use the buffer are
+// enqueued, so that another host thread on the same stream cannot free it in
+// between (its synchronisation would not cover kernels not yet enqueued).
 std::mutex g_ws_mutex;
 std::map<std::pair<int, uintptr_t>, std::pair<void*, size_t>> g_ws;
 
-dg_status get_workspace(size_t bytes, hipStream_t stream, float** out) {
+dg_status get_workspace(size_t bytes, hipStream_t stream, float** out, std::unique_lock<std::mutex>& lock) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  lock = std::unique_lock<std::mutex>(g_ws_mutex);
   auto& ent = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
   if (ent.second < bytes) {
     if (ent.first != nullptr) {
@@ -258,6 +261,7 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, bool e8m
   if (st != DG_SUCCESS) return st;
   const int slots = cus * cfg.per_cu;
   bool split = false;
+  std::unique_lock<std::mutex> ws_lock;  // held until the split launches are enqueued
   if (MODE == dg::MODE_DENSE && (cfg.id == TILE_SK_128x64 || cfg.id == TILE_SK_64x128) && p.k >= 128 * 8) {
     int sps = 0;
     int s = choose_splits(p.tiles_m * p.tiles_n, p.k / 128, slots, &sps);
@@ -271,7 +275,7 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, bool e8m
       p.splits = s;
       p.slabs_per_split = sps;
       p.ldw = (p.n + 3) / 4 * 4;
-      st = get_workspace(static_cast<size_t>(s) * p.m * p.ldw * sizeof(float), stream, &p.ws);
+      st = get_workspace(static_cast<size_t>(s) * p.m * p.ldw * sizeof(float), stream, &p.ws, ws_lock);
       if (st != DG_SUCCESS) return st;
     }
   }

@@ -249,3 +249,41 @@ def test_split_k_determinism_and_sentinel_columns():
     d2 = run_dense(x, ld_d=2120)
     assert np.array_equal(raw_bits(d1), raw_bits(d2))
     _check_dense(x, d1, "split-K M=64 N=2112 K=7168")
+
+
+def test_split_k_threads_sharing_a_stream():
+    """Two host threads issue skinny (split-K) calls of different shapes on one fresh
+    stream: each call's GEMM and reduction use the stream's workspace as one unit (the
+    workspace grows on the way), so every output equals the single-threaded result."""
+    import threading
+
+    xs = [gen_dense(64, 2112, 7168, seed=70), gen_dense(100, 1040, 4096, seed=71)]
+    want = [raw_bits(run_dense(x)) for x in xs]
+    dev = [(fp8_dev(x["a"]), to_dev(x["sfa"]), fp8_dev(x["b"]), to_dev(x["sfb"])) for x in xs]
+    s = torch.cuda.Stream()
+    calls = 24
+    outs = [[out_buffer((x["m"],), x["n"], x["out_dtype"]) for _ in range(calls)] for x in xs]
+    torch.cuda.synchronize()  # inputs and sentinel fills are on the default stream
+    start = threading.Barrier(2)
+    errors = []
+
+    def worker(i):
+        try:
+            a, sfa, b, sfb = dev[i]
+            start.wait()
+            with torch.cuda.stream(s):
+                for d in outs[i]:
+                    dg.fp8_gemm_nt((a, sfa), (b, sfb), d)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for j, d in enumerate(outs[i]):
+            assert np.array_equal(raw_bits(d), want[i]), f"input {i}, call {j}"
