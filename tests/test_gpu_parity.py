@@ -83,6 +83,21 @@ def test_dense_ragged_shapes(m, n, k):
     _check_dense(x, d, f"dense ragged M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m,n,k,fmt", [(300, 1005, 256, "fp32"), (300, 13, 384, "fp32"), (520, 2110, 512, "fp32"),
+                                       (300, 1005, 256, "ue8m0"), (260, 229, 384, "fp32")])
+def test_dense_bf16_ragged_n_columns(m, n, k, fmt):
+    """BF16 output with N not a multiple of 8 (16-byte stores of eight columns fall back
+    to element stores at the edge) and a padded leading dimension: values match the
+    oracle and the padding columns past N keep the sentinel."""
+    ld = (n + 7) // 8 * 8 + 8
+    x = gen_dense(m, n, k, seed=7 * n + k, scale_fmt=fmt)
+    d = run_dense(x, ld_d=ld)
+    ref = (oracle.ref_dense_ue8m0 if fmt == "ue8m0" else oracle.ref_dense)(x["a"], x["sfa"], x["b"], x["sfb"])
+    oracle.assert_close(as_f64(d), ref, f"bf16 ragged N m={m} n={n} k={k} {fmt}")
+    full = d.as_strided((m, ld), (ld, 1))  # d is the first n columns of an [m, ld] buffer
+    assert (raw_bits(full)[:, n:] == sentinel_of(d)).all(), "columns past N were written"
+
+
 def test_dense_padded_sfa_and_k_zero():
     x = gen_dense(70, 64, 256, seed=3, ld_sfa=96)
     x["sfa"][:, 70:] = np.nan  # padding columns must never be read into valid rows
