@@ -170,6 +170,23 @@ __device__ __forceinline__ void raster(int t, int tm, int tn, int& mb, int& nb) 
   nb = r / gsz;
 }
 
+// v += C[row][gn .. gn+3] for a BF16 C (FP32 add), columns past N skipped.
+// crow = element offset of the row in C.
+__device__ __forceinline__ void add_c_bf16(const Params& p, int64_t crow, int gn, f32x4& v) {
+  const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
+  if (gn + 4 <= p.n) {  // 8-byte aligned: the row stride is a multiple of 16 bytes and gn of 4
+    const uint2 cv = *reinterpret_cast<const uint2*>(C);
+    v[0] += __uint_as_float(cv.x << 16);
+    v[1] += __uint_as_float(cv.x & 0xFFFF0000u);
+    v[2] += __uint_as_float(cv.y << 16);
+    v[3] += __uint_as_float(cv.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
+  }
+}
+
 // D[row][gn .. gn+3] = C + v (FP32 add, one rounding), columns past N dropped.
 // crow / drow = element offsets of the row in C / D.
 template <bool BF16_OUT, bool HAS_C>
@@ -177,10 +194,7 @@ __device__ __forceinline__ void store_out(const Params& p, int64_t crow, int gn,
   const bool full = gn + 4 <= p.n;
   if (HAS_C) {
     if (BF16_OUT) {
-      const uint16_t* C = reinterpret_cast<const uint16_t*>(p.c) + crow + gn;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (full || gn + r < p.n) v[r] += __uint_as_float((uint32_t)C[r] << 16);
+      add_c_bf16(p, crow, gn, v);
     } else {
       const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
       if (full) {
@@ -459,8 +473,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   // counter); letting the stores stay in flight past it, with counted waits,
   // measured 1 % slower on full 256-row tiles.
   constexpr bool XPRE = STAGES == 2;
-  // BF16 output without C: paired 16-byte stores (see the epilogue)
-  constexpr bool PAIRED_STORES = BF16_OUT && !HAS_C && !SPLIT;
+  // BF16 output: paired 16-byte stores (see the epilogue)
+  constexpr bool PAIRED_STORES = BF16_OUT && !SPLIT;
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   Unit u = find_unit(vb, 0), nx;
@@ -712,6 +726,13 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
               // row_ok; the swaps run before the row test, on the whole wave.
 #pragma unroll
               for (int j = 0; j + 1 < FN; j += 2) {
+                if (HAS_C && row_ok) {  // C in the MFMA layout: this lane's row, columns 4 * q4 ..
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    const int gc = n0 + wn * TN + (j + h) * 16 + 4 * q4;
+                    if (gc < p.n) add_c_bf16(p, crow, gc, acc[i][j + h]);
+                  }
+                }
                 const auto s0 = __builtin_amdgcn_permlane16_swap(bf16x2_rne_bits(acc[i][j][0], acc[i][j][1]),
                                                                  bf16x2_rne_bits(acc[i][j + 1][0], acc[i][j + 1][1]),
                                                                  false, false);
