@@ -1,17 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the fine-grained-scaled FP8 GEMM library on one MI355X.
 
-One step = one pass of the selected workload (default: the 15-shape dense
-sweep, M in {64, 128, 4096} x (N, K) in {(2112,7168), (24576,1536),
-(7168,16384), (4096,7168), (7168,2048)}, BF16 out) through the library's
-C ABI, with inputs already resident in HBM.  Prints ONE JSON line:
+One step = one pass of the selected workload through the library's C ABI,
+with inputs already resident in HBM.  The default workload ("baseline") is
+the five benchmark configurations, 19 calls: (0) dense M=128 N=256 K=512;
+(1) the 15-shape dense sweep, M in {64, 128, 4096} x (N, K) in {(2112,7168),
+(24576,1536), (7168,16384), (4096,7168), (7168,2048)}; (2) the contiguous MoE
+GEMM, 8 groups of U[1,8192] tokens, N=4096 K=7168; (3) masked decode, 16
+groups of U[0,256] rows, (N,K) in {(4096,7168), (7168,2048)}; (4) dense
+M=N=8192 K=16384 with FP32 C and D.  BF16 out except (4).  Prints ONE JSON line:
 
   value        whole-job FP8 TFLOPS = algorithmic flops of the step / wall time
   roofline     the dominant launch (largest per-launch time) against the MI355X
                dense-FP8 MFMA peak (or HBM bandwidth when that binds), timed
                with HIP events on the stream the library launches on
   cpu_baseline the FP64 CPU oracle on a bounded sample of the same workload
-  detail       per-shape TFLOPS and roofline fractions
+  detail       per-shape cold/warm times, TFLOPS and roofline fractions, and per
+               configuration the cold TFLOPS (sum of flops / sum of cold times)
 
 Algorithmic work counts only what the method must do: flops 2*N*K per valid
 row; bytes = A (valid rows) + B (groups with valid rows) + scales + D (valid
@@ -304,6 +309,7 @@ class Case:
         import moe_grouped_gemm_tiles_amd as dg
 
         self.label = desc["label"]
+        self.config = desc.get("config")
         self.x = x = desc["gen"]()
         self.flops, self.bytes = algorithmic_work(x)
 
@@ -349,7 +355,8 @@ class Case:
         elif x["kind"] == "dense":
             d = torch.empty(x["m"], x["n"], dtype=dt, device=dev)
             c = up(x["c"]).to(dt) if x.get("c") is not None else None
-            self.call = lambda: dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c)
+            ws = dg.alloc_workspace(x["m"], x["n"], x["k"], dev)  # kept by the caller, cleared once
+            self.call = lambda: dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c, workspace=ws)
         elif x["kind"] == "contiguous":
             d = torch.empty(x["m_total"], x["n"], dtype=dt, device=dev)
             mi = up(x["m_indices"])
@@ -460,7 +467,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="dense_sweep")
+    ap.add_argument("--workload", default="baseline")
     ap.add_argument("--cases", default="", help="comma-separated case indices of the workload to keep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=512, help="cache flush buffer for the per-shape cold timing")
@@ -525,7 +532,7 @@ def main():
         warm = time_launches(c, args.timing_iters)
         cold = time_launches(c, args.timing_iters, flush)
         c.warm_s, c.cold_s = warm, cold
-        detail.append(dict(case=c.label, bound=c.bound, tflops_cold=c.flops / cold / 1e12,
+        detail.append(dict(case=c.label, config=c.config, bound=c.bound, tflops_cold=c.flops / cold / 1e12,
                            tflops_warm=c.flops / warm / 1e12, us_cold=cold * 1e6, us_warm=warm * 1e6,
                            roofline_frac_cold=c.roof_s / cold, roofline_frac_warm=c.roof_s / warm))
         print(f"bench:   {c.label}: cold {cold * 1e6:.1f} us ({c.flops / cold / 1e12:.1f} TFLOPS, "
@@ -600,13 +607,28 @@ def main():
                  + ("UE8M0 power-of-two" if cases[0].x.get("scale_fmt") == "ue8m0" else "FP32") + " scales)")
                 if step_flops > 0 else "synthetic (seeded N(0,1) rows with e^U(-4,4) magnitude spread, BF16)",
         "config": {"workload": args.workload, "cases": [c.label for c in cases],
-                   "out_dtype": cases[0].x.get("out_dtype", "fp32")},
+                   "out_dtype": sorted({c.x.get("out_dtype", "fp32") for c in cases if "out_dtype" in c.x})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
     }
     if step_flops > 0:
         out["config"]["pct_of_fp8_peak"] = 100.0 * value / PEAK_FP8_TFLOPS
+    groups = {}
+    for c in cases:
+        if c.config is not None:
+            groups.setdefault(c.config, []).append(c)
+    if groups:
+        out["config"]["configs"] = {str(g): [c.label for c in cs] for g, cs in sorted(groups.items())}
+        summ = {}
+        for g, cs in sorted(groups.items()):
+            fl = sum(c.flops for c in cs)
+            cold = sum(c.cold_s for c in cs)
+            roof = sum(c.roof_s for c in cs)
+            summ[str(g)] = dict(cases=len(cs), tflops_cold=fl / cold / 1e12, us_cold=cold * 1e6,
+                                roofline_frac_cold=roof / cold,
+                                bound="+".join(sorted({c.bound for c in cs})))
+        out["summary_by_config"] = summ
     print(json.dumps(out), flush=True)
 
 

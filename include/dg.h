@@ -18,9 +18,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library keeps no pointer after the call returns.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
- *     Nothing synchronises with the host; entry points are safe to capture
- *     into a HIP graph once the library has run the same configuration
- *     outside capture (see "Workspace" below).
+ *     Nothing synchronises with the host and the library allocates no
+ *     memory, so every entry point may be captured into a HIP graph.
  *   - Scale layouts:
  *       sfa: FP32 [K/128][ld_sfa], transposed ("MN-major"): sfa[kb*ld_sfa + m]
  *            scales A[m, kb*128 .. kb*128+127].  ld_sfa >= rows of A and
@@ -40,15 +39,22 @@
  *     never an error: out-of-range values are clamped or skipped so that all
  *     memory accesses stay in bounds.
  *
- * Workspace: skinny dense GEMMs (M <= 128, K >= 1024) split K across
- * workgroups.  Their FP32 partial sums go to a workspace the library keeps
- * per (device, stream): allocated with hipMalloc the first time a shape on
- * that stream needs it, grown (after synchronising that stream) when a larger
- * shape needs more, kept until process exit.  Calls under graph capture must
- * therefore be preceded by one uncaptured call of the same shape on the
- * capture stream; a captured graph uses that stream's workspace.  Host
- * threads may share a stream: the workspace stays locked from its lookup until
- * the call's kernels are enqueued.
+ * Workspace: skinny dense GEMMs (M <= 128, K >= 512) split K across
+ * workgroups.  Each workgroup writes the FP32 partial sum of its K range to a
+ * caller-owned workspace and counts itself in a per-tile counter there; the
+ * workgroup that completes a tile adds the partials in K-range order (so the
+ * result is deterministic), writes D and resets the counter.  One launch per
+ * call.  The workspace:
+ *   - size: dg_get_workspace_size(m, n, k) bytes (0 = the call needs none and
+ *     may pass NULL); the size depends on the shape and on the CU count in use
+ *     (dg_set_num_cus), so query it with the same settings as the call;
+ *   - device memory, 256-byte aligned, ZERO-FILLED before its first use; every
+ *     call leaves it ready for the next one (its counters back at zero), so it
+ *     is cleared once, not per call;
+ *   - owned by the caller: the library keeps no pointer to it.  Calls that
+ *     share one workspace must not overlap (order them on one stream); calls
+ *     on concurrent streams need workspaces of their own.
+ * A missing, misaligned or too small workspace -> DG_ERROR_WORKSPACE.
  */
 #ifndef DG_H
 #define DG_H
@@ -65,7 +71,7 @@ typedef enum {
   DG_ERROR_INVALID_VALUE = 1,  /* null/misaligned pointer, bad stride, negative size, bad enum */
   DG_ERROR_NOT_SUPPORTED = 2,  /* valid but unsupported: K % 128 != 0, contiguous M % 128 != 0 */
   DG_ERROR_LAUNCH_FAILED = 3,  /* a HIP call failed; hipGetLastError() text via dg_last_hip_error */
-  DG_ERROR_OUT_OF_MEMORY = 4   /* workspace allocation failed */
+  DG_ERROR_WORKSPACE = 4       /* split-K workspace NULL, misaligned or smaller than dg_get_workspace_size */
 } dg_status;
 
 typedef enum { DG_DTYPE_BF16 = 0, DG_DTYPE_FP32 = 1 } dg_dtype;
@@ -85,11 +91,26 @@ typedef enum { DG_DTYPE_BF16 = 0, DG_DTYPE_FP32 = 1 } dg_dtype;
  * d      output, dtype d_dtype, row stride ldd elements, ldd >= n, rows 16-B aligned.
  * m,n,k  sizes; m == 0 or n == 0 -> DG_SUCCESS with nothing enqueued;
  *        k == 0 -> D = C (or 0); k % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
+ * workspace, workspace_bytes
+ *        split-K workspace (see "Workspace" above); NULL and 0 when
+ *        dg_get_workspace_size(m, n, k) is 0.
  */
 dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
                          const void* b, int64_t ldb, const float* sfb,
                          const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
-                         int m, int n, int k, hipStream_t stream);
+                         int m, int n, int k, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Bytes of split-K workspace the dense GEMMs (dg_fp8_gemm_nt, its UE8M0 form
+ * and dg_wgrad_fp8_gemm_nt) need for an M x N x K call on the current device
+ * with the current CU cap; 0 when the call does not split K (M > 128, K < 512)
+ * or the sizes are invalid.  One workspace serves calls of several shapes
+ * if it is at least as large as each call's size.  Host-only, enqueues nothing.
+ *   (The pages leave the workspace of split reductions unspecified; the
+ *   README's calls take caller-allocated outputs, "Mega MoE" usage.)
+ */
+size_t dg_get_workspace_size(int m, int n, int k);
 
 /*
  * M-grouped GEMM, contiguous layout (MoE prefill / training forward):
@@ -111,7 +132,7 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
  * m_total % 128 != 0 -> DG_ERROR_NOT_SUPPORTED.
  * The call enqueues one kernel, or two on the same stream when the last round
  * of 256-row tiles would keep at most half the CUs busy (its rows then go to
- * 128x128 tiles; same bits).  DG_TAIL_SPLIT=0 in the environment keeps one.
+ * 128x128 tiles; same bits).
  */
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa,
                                               const void* b, const float* sfb,
@@ -161,7 +182,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
 dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t ld_sfa,
                                const void* b, int64_t ldb, const int32_t* sfb,
                                const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
-                               int m, int n, int k, hipStream_t stream);
+                               int m, int n, int k, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
                                                     const void* b, const int32_t* sfb,
                                                     void* d, dg_dtype d_dtype,
@@ -211,11 +233,12 @@ dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, i
  *   dg_wgrad_fp8_gemm_nt            D[m,n] += A[m,k] @ B[n,k]^T           (dense)
  *   dg_k_grouped_wgrad_fp8_gemm_nt  D[g]   += A[:, K_g] @ B[:, K_g]^T      (K-grouped)
  * They are dg_fp8_gemm_nt with c = d (FP32) and dg_k_grouped_fp8_gemm_nt_contiguous
- * with c = d; arguments as there.
+ * with c = d; arguments as there (the dense one takes the split-K workspace).
  */
 dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
                                const void* b, int64_t ldb, const float* sfb,
-                               float* d, int64_t ldd, int m, int n, int k, hipStream_t stream);
+                               float* d, int64_t ldd, int m, int n, int k,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_t ld_sfa,
                                          const void* b, const float* sfb, float* d, const int32_t* ks,
                                          int num_groups, int m, int n, int k_total, hipStream_t stream);
@@ -331,20 +354,12 @@ int64_t dg_get_sf_aligned_size(int64_t mn);
 
 /* Cap on compute units the kernels spread over (0 = all CUs of the current
  * device, the default; DG_NUM_CUS in the environment sets the initial value).
- * Negative -> DG_ERROR_INVALID_VALUE.  Process-wide.
+ * Negative -> DG_ERROR_INVALID_VALUE.  Process-wide.  dg_get_num_cus returns
+ * the CUs the kernels use on the current device (the cap, or all CUs when
+ * uncapped); without a usable device it returns the cap (0 = uncapped).
  * [README] "Utilities": set_num_sms / get_num_sms. */
 dg_status dg_set_num_cus(int num_cus);
 int dg_get_num_cus(void);
-
-/* Tuning knob: width of the 256-row output tiles the large-M kernels use.
- * 0 (default; DG_TILE_N in the environment sets the initial value) picks per
- * call among 256, 224 and 160 columns the width with the fewest workgroup
- * rounds times tile width (narrower tiles even out the last round on the
- * CUs, e.g. N = 7168); 256, 224 or 160 forces that width.  Other values ->
- * DG_ERROR_INVALID_VALUE.  Process-wide; results agree to the stated
- * tolerance whatever the width (the K order of every output is unchanged). */
-dg_status dg_set_tile_n(int tile_n);
-int dg_get_tile_n(void);
 
 /* Static text for a status code (never NULL). */
 const char* dg_status_string(dg_status s);

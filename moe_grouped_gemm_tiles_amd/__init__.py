@@ -7,7 +7,7 @@ arithmetic runs in the HIP kernels; PyTorch only provides device memory and
 the stream.  Names mirror the DeepGEMM README ("Interfaces", "Utilities")
 as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
 
-* ``fp8_gemm_nt((a, sfa), (b, sfb), d, c=None)``
+* ``fp8_gemm_nt((a, sfa), (b, sfb), d, c=None, workspace=None)``
 * ``m_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, m_indices)``
 * ``m_grouped_fp8_gemm_nt_masked((a, sfa), (b, sfb), d, masked_m, expected_m)``
 * ``k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c=None)``
@@ -18,7 +18,15 @@ as mirrored on the page "Weight gradient kernels for dense and MoE models #95":
 * ``fp8_mqa_logits(q, (kv, kv_sf), weights, ks, ke, clean_logits, out)``
   (README "V3.2 MQA kernels for the indexer")
 * ``get_mk_alignment_for_contiguous_layout()``, ``get_sf_aligned_size(mn)``,
-  ``set_num_cus(n)`` / ``get_num_cus()``, ``set_tile_n(w)`` / ``get_tile_n()``
+  ``set_num_cus(n)`` / ``get_num_cus()``, ``get_workspace_size(m, n, k)`` and
+  ``alloc_workspace(m, n, k)``
+
+Skinny dense GEMMs (M <= 128) split K across workgroups and need a split-K
+workspace (``get_workspace_size``): zero-filled device memory that the caller
+keeps and passes to every call (``alloc_workspace`` makes one); each call
+leaves it ready for the next.  Without one, the dense calls take a fresh
+workspace from torch's allocator per call and clear its counters (one small
+fill kernel before the GEMM).
 
 The three M-side GEMMs take either FP32 scales or UE8M0 scales packed four
 per int32 along K (the README's "Interfaces > Notices" names both formats);
@@ -59,8 +67,8 @@ __all__ = [
     "get_sf_aligned_size",
     "set_num_cus",
     "get_num_cus",
-    "set_tile_n",
-    "get_tile_n",
+    "get_workspace_size",
+    "alloc_workspace",
     "set_num_sms",
     "get_num_sms",
     "get_tma_aligned_size",
@@ -78,23 +86,26 @@ _STATUS = {0: "DG_SUCCESS"}
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int
+_sz = ctypes.c_size_t
 
 _SIGNATURES = {
     "dg_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
-                              _i32, _i32, _i32, _vp]),
+                              _i32, _i32, _i32, _vp, _sz, _vp]),
+    "dg_get_workspace_size": (_sz, [_i32, _i32, _i32]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                    _i32, _i32, _i32, _i32, _vp]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _vp]),
     "dg_fp8_gemm_nt_ue8m0": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
-                                    _i32, _i32, _i32, _vp]),
+                                    _i32, _i32, _i32, _vp, _sz, _vp]),
     "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                          _i32, _i32, _i32, _i32, _vp]),
     "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                      _i32, _i32, _i32, _i32, _i32, _vp]),
     "dg_k_grouped_fp8_gemm_nt_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                                    _i32, _i32, _i32, _i32, _vp]),
-    "dg_wgrad_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "dg_wgrad_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _sz,
+                                    _vp]),
     "dg_k_grouped_wgrad_fp8_gemm_nt": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                                          _i32, _i32, _i32, _i32, _vp]),
@@ -108,8 +119,7 @@ _SIGNATURES = {
     "dg_get_sf_aligned_size": (_i64, [_i64]),
     "dg_set_num_cus": (_i32, [_i32]),
     "dg_get_num_cus": (_i32, []),
-    "dg_set_tile_n": (_i32, [_i32]),
-    "dg_get_tile_n": (_i32, []),
+    "dg_internal_set_tile_n": (_i32, [_i32]),
     "dg_status_string": (ctypes.c_char_p, [_i32]),
     "dg_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -213,8 +223,42 @@ def _dense_contig(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
-def fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, c: torch.Tensor | None = None):
-    """D = C + A @ B.T with A [M,K], B [N,K] E4M3 and FP32 or packed-UE8M0 fine-grained scales."""
+def get_workspace_size(m: int, n: int, k: int) -> int:
+    """Bytes of split-K workspace a dense M x N x K call needs on the current device (0: none)."""
+    return int(load_library().dg_get_workspace_size(m, n, k))
+
+
+def alloc_workspace(m: int, n: int, k: int, device=None) -> torch.Tensor | None:
+    """A zero-filled split-K workspace for dense M x N x K calls (None when they need none).
+    Keep it and pass it to every call of that shape; calls sharing it must not overlap."""
+    size = get_workspace_size(m, n, k)
+    if size == 0:
+        return None
+    return torch.zeros(size, dtype=torch.uint8, device=device if device is not None else torch.cuda.current_device())
+
+
+_WS_ALIGN = 256  # the library's alignment rule for workspaces
+
+
+def _workspace(m: int, n: int, k: int, workspace: torch.Tensor | None, like: torch.Tensor):
+    """(pointer, bytes) of the split-K workspace for a dense call; without one, a fresh
+    zero-filled workspace from torch's allocator (filled on the current stream)."""
+    size = get_workspace_size(m, n, k)
+    if size == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.zeros(size + _WS_ALIGN, dtype=torch.uint8, device=like.device)
+        off = (-workspace.data_ptr()) % _WS_ALIGN
+        workspace = workspace[off:off + size]
+    elif not workspace.is_cuda or workspace.device != like.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the output's device")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, c: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """D = C + A @ B.T with A [M,K], B [N,K] E4M3 and FP32 or packed-UE8M0 fine-grained scales.
+    ``workspace``: split-K workspace for skinny M (``alloc_workspace``), or None."""
     lib = load_library()
     a, sfa = a_pair
     b, sfb = b_pair
@@ -237,8 +281,9 @@ def fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, c: torch.Tensor | None = None):
         c_ptr, ldc = c.data_ptr(), _ld(c, 0, 16 // c.element_size())
     fn = lib.dg_fp8_gemm_nt_ue8m0 if ue else lib.dg_fp8_gemm_nt
     es = d.element_size()
+    ws, ws_bytes = _workspace(m, n, k, workspace, d)
     st = fn(a.data_ptr(), _ld(a, 0, 16), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(), _ld(b, 0, 16),
-            sfb.data_ptr(), c_ptr, ldc, d.data_ptr(), _ld(d, 0, 16 // es), dt, m, n, k, _stream(d))
+            sfb.data_ptr(), c_ptr, ldc, d.data_ptr(), _ld(d, 0, 16 // es), dt, m, n, k, ws, ws_bytes, _stream(d))
     _check(st)
     return d
 
@@ -292,7 +337,9 @@ def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d: torch.Tensor, masked_m: torc
     if sfa.dim() != 3 or sfa.shape[:2] != (g, kr) or sfb.shape != (g, (n + 127) // 128, kr):
         raise ValueError("scale shape mismatch")
     fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if ue else lib.dg_m_grouped_fp8_gemm_nt_masked
-    st = fn(a.data_ptr(), sfa.data_ptr(), _ld(sfa, 1, 4), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
+    # sfa is contiguous [G, rows, L]: the library steps groups by rows * L, so L itself
+    # (not a rounded-up stride) is the leading dimension it must validate
+    st = fn(a.data_ptr(), sfa.data_ptr(), sfa.shape[2], b.data_ptr(), sfb.data_ptr(), d.data_ptr(), dt,
             masked_m.data_ptr(), g, m_max, n, k, int(expected_m), _stream(d))
     _check(st)
     return d
@@ -339,8 +386,9 @@ def k_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d: torch.Tensor, ks: torch.
     return d
 
 
-def wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor):
-    """Dense weight gradient: D += A @ B.T in FP32 (D is read and written)."""
+def wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor, workspace: torch.Tensor | None = None):
+    """Dense weight gradient: D += A @ B.T in FP32 (D is read and written).
+    ``workspace``: split-K workspace for skinny M (``alloc_workspace``), or None."""
     lib = load_library()
     a, sfa = a_pair
     b, sfb = b_pair
@@ -357,8 +405,10 @@ def wgrad_fp8_gemm_nt(a_pair, b_pair, d: torch.Tensor):
         raise ValueError("shape mismatch")
     if sfa.dim() != 2 or sfa.shape[0] != k // 128 or sfb.shape != ((n + 127) // 128, k // 128):
         raise ValueError("scale shape mismatch")
+    ws, ws_bytes = _workspace(m, n, k, workspace, d)
     st = lib.dg_wgrad_fp8_gemm_nt(a.data_ptr(), _ld(a, 0, 16), sfa.data_ptr(), _ld(sfa, 0, 4), b.data_ptr(),
-                                  _ld(b, 0, 16), sfb.data_ptr(), d.data_ptr(), _ld(d, 0, 4), m, n, k, _stream(d))
+                                  _ld(b, 0, 16), sfb.data_ptr(), d.data_ptr(), _ld(d, 0, 4), m, n, k, ws, ws_bytes,
+                                  _stream(d))
     _check(st)
     return d
 
@@ -486,13 +536,10 @@ def get_num_cus() -> int:
     return load_library().dg_get_num_cus()
 
 
-def set_tile_n(w: int):
-    """Force the width of the 256-row tiles (256, 224 or 160; 0 = automatic)."""
-    _check(load_library().dg_set_tile_n(w))
-
-
-def get_tile_n() -> int:
-    return load_library().dg_get_tile_n()
+def _set_tile_n_for_tests(w: int):
+    """Force the width of the 256-row tiles (256, 224 or 160; 0 = chosen per call).
+    Not part of the API: the tests use it to cover every tile width."""
+    _check(load_library().dg_internal_set_tile_n(w))
 
 
 # The README's names for the same utilities ("Utilities": set_num_sms / get_num_sms cap the

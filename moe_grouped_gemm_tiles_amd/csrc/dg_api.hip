@@ -14,39 +14,34 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
 #include <mutex>
-#include <utility>
 
 #include "dg.h"
 #include "dg_common.hpp"
+#include "dg_internal.h"
 #include "dg_kernels.hpp"
 
 namespace {
 
 constexpr int kAlignM = 128;
 constexpr int kMaxDevices = 64;
-
+// Split-K workspace layout: kCtrWords tile counters (zero between calls), then
+// the FP32 partial tiles.  The counters sit at a fixed place so that calls of
+// different shapes sharing one workspace never read partials as counters.
+constexpr int kCtrWords = 16384;
+constexpr size_t kCtrBytes = kCtrWords * sizeof(uint32_t);
+constexpr size_t kWorkspaceAlign = 256;
 
 std::atomic<int> g_num_cus{-1};  // -1: not yet read from the environment
 int g_device_cus[kMaxDevices] = {0};
 std::once_flag g_env_once;
 bool g_print_configs = false;
-int g_force_splits = 0;
-bool g_tail_split = true;  // DG_TAIL_SPLIT=0 keeps the ragged last round of contiguous calls
-std::atomic<int> g_tile_n{0};  // forced width of the 256-row tiles (0 = automatic)
+std::atomic<int> g_tile_n{0};  // forced width of the 256-row tiles (0 = automatic; tests only)
 
 void read_env() {
   std::call_once(g_env_once, [] {
     const char* s = std::getenv("DG_PRINT_CONFIGS");
     g_print_configs = s && std::atoi(s) != 0;
-    const char* f = std::getenv("DG_FORCE_SPLITS");
-    g_force_splits = f ? std::atoi(f) : 0;
-    const char* ts = std::getenv("DG_TAIL_SPLIT");
-    g_tail_split = !(ts && std::atoi(ts) == 0);
-    const char* tn = std::getenv("DG_TILE_N");
-    const int w = tn ? std::atoi(tn) : 0;
-    if (w == 256 || w == 224 || w == 160) g_tile_n.store(w);
     int expected = -1;
     const char* c = std::getenv("DG_NUM_CUS");
     const int v = c ? std::atoi(c) : 0;
@@ -104,25 +99,24 @@ constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
 constexpr Cfg kCfgSk128{TILE_SK_128x64, 128, 64, 2, 2, 3, 2};
 constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 3, 2};
 
-// Output flavour of a launch: split-K partials, or the final D with or without C.
+// Output flavour of a launch.
 struct Epi {
-  bool split, bf16, has_c, e8m0;
+  bool bf16, has_c, e8m0;
 };
 
 // Only the combinations the entry points can reach are instantiated:
-// dense: every tile, BF16/FP32, with/without C, split partials for the skinny
-// tiles; M-grouped: 256x256 and 128x128 without C; K-grouped: FP32 with/without C.
+// dense: every tile, BF16/FP32, with/without C (the skinny tiles split K);
+// M-grouped: the 256-row tiles and 128x128 without C; K-grouped: FP32
+// with/without C.
 template <int BM, int BN, int WM, int WN, int ST, int MODE, bool E8M0>
 KernelFn pick_out(const Epi& e) {
-  constexpr bool kSkinny = BM < 128 || BN < 128;
+  constexpr bool kSplit = MODE == dg::MODE_DENSE && (BM < 128 || BN < 128);
   if constexpr (MODE == dg::MODE_DENSE) {
-    if constexpr (kSkinny)
-      if (e.split) return dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, true, false, false, E8M0>;
     if (e.bf16)
-      return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, true, E8M0>
-                     : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false, E8M0>;
-    return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true, E8M0>
-                   : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
+      return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, kSplit, true, true, E8M0>
+                     : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, kSplit, true, false, E8M0>;
+    return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, kSplit, false, true, E8M0>
+                   : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, kSplit, false, false, E8M0>;
   } else if constexpr (MODE == dg::MODE_KGROUP) {
     return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, true, E8M0>
                    : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
@@ -130,11 +124,6 @@ KernelFn pick_out(const Epi& e) {
     return e.bf16 ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, true, false, E8M0>
                   : dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, false, false, false, E8M0>;
   }
-}
-
-KernelFn pick_reduce(dg_dtype t, bool has_c) {
-  if (t == DG_DTYPE_BF16) return has_c ? dg::splitk_reduce_kernel<true, true> : dg::splitk_reduce_kernel<true, false>;
-  return has_c ? dg::splitk_reduce_kernel<false, true> : dg::splitk_reduce_kernel<false, false>;
 }
 
 template <int MODE, bool E8M0>
@@ -157,43 +146,6 @@ KernelFn pick_kernel(const Cfg& c, const Epi& e) {
 const char* mode_name(int mode) {
   return mode == dg::MODE_DENSE ? "dense" : mode == dg::MODE_CONTIG ? "contiguous"
        : mode == dg::MODE_MASKED ? "masked" : "k-grouped";
-}
-
-// ---- split-K workspace: one growable FP32 buffer per (device, stream) --------
-// Kernels on one stream run in order, so one buffer per stream is race-free.
-// Growing it synchronises that stream before freeing the old buffer; this is
-// the only allocation the library makes and it happens outside the kernels.
-// The caller keeps `lock` held until its kernels that use the buffer are
-// enqueued, so that another host thread on the same stream cannot free it in
-// between (its synchronisation would not cover kernels not yet enqueued).
-std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, std::pair<void*, size_t>> g_ws;
-
-dg_status get_workspace(size_t bytes, hipStream_t stream, float** out, std::unique_lock<std::mutex>& lock) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e);
-  lock = std::unique_lock<std::mutex>(g_ws_mutex);
-  auto& ent = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
-  if (ent.second < bytes) {
-    if (ent.first != nullptr) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return hip_fail(e);
-      e = hipFree(ent.first);
-      if (e != hipSuccess) return hip_fail(e);
-      ent = {nullptr, 0};
-    }
-    const size_t want = bytes + bytes / 2;
-    void* ptr = nullptr;
-    e = hipMalloc(&ptr, want);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return DG_ERROR_OUT_OF_MEMORY;
-    }
-    ent = {ptr, want};
-  }
-  *out = static_cast<float*>(ent.first);
-  return DG_SUCCESS;
 }
 
 // Width of the 256-row tiles: the candidate with the least (workgroup rounds x
@@ -224,19 +176,22 @@ Cfg choose_wide(int64_t row_tiles, int n, int slots) {
   return best;
 }
 
-// Split count for a skinny dense GEMM: minimise (workgroup rounds x slabs per
-// split), lightly penalising every extra split (its FP32 partial costs
-// traffic), with at least 4 slabs per split.
-int choose_splits(int tiles, int kb, int slots, int* slabs_per_split) {
+// Split count for a skinny dense GEMM.  Estimated time, in slab times: rounds
+// of units at one unit per CU x (slabs per split + ~6 slabs of pipeline fill
+// and latency per unit), plus ~0.5 slab time per extra split for the partials
+// the last unit of each tile reads back.  Fitted to cold timings of the
+// dense-sweep shapes with M <= 128 over forced split counts 1..32: the best
+// counts keep about one unit per CU (a second unit on a CU shares its memory
+// pipeline) and stop short of many small splits.
+int choose_splits(int tiles, int kb, int cus, int* slabs_per_split) {
   int best_s = 1, best_sps = kb;
   double best_cost = 1e300;
-  const int max_s = kb / 4 > 1 ? kb / 4 : 1;
-  for (int s = 1; s <= max_s; ++s) {
+  for (int s = 1; s <= kb; ++s) {
     const int sps = cdiv(kb, s);
     const int s_eff = cdiv(kb, sps);
-    const int units = tiles * s_eff;
-    const int rounds = cdiv(units, slots);
-    const double cost = static_cast<double>(rounds) * sps * (1.0 + 0.03 * (s_eff - 1));
+    if (s_eff != s) continue;
+    const int rounds = cdiv(tiles * s_eff, cus);
+    const double cost = static_cast<double>(rounds) * (sps + 6.0) + 0.5 * (s_eff - 1);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best_s = s_eff;
@@ -247,42 +202,56 @@ int choose_splits(int tiles, int kb, int slots, int* slabs_per_split) {
   return best_s;
 }
 
+// Tile configuration and K split of a dense call, and the workspace the split needs.
+struct DensePlan {
+  Cfg cfg;
+  int splits, slabs_per_split;
+  size_t ws_bytes;  // 0: no split, no workspace
+};
+
+dg_status plan_dense(int m, int n, int k, DensePlan* out) {
+  int cus = 0;
+  dg_status st = usable_cus(&cus);
+  if (st != DG_SUCCESS) return st;
+  DensePlan pl{};
+  pl.cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? choose_wide(cdiv(m, 256), n, cus) : kCfg128);
+  pl.splits = 1;
+  pl.slabs_per_split = k / 128;
+  pl.ws_bytes = 0;
+  const bool skinny = pl.cfg.id == TILE_SK_128x64 || pl.cfg.id == TILE_SK_64x128;
+  const int64_t tiles = static_cast<int64_t>(cdiv(m, pl.cfg.bm)) * cdiv(n, pl.cfg.bn);
+  if (skinny && k >= 128 * 2 && tiles > 0 && tiles <= kCtrWords) {
+    int sps = 0;
+    const int s = choose_splits(static_cast<int>(tiles), k / 128, cus, &sps);
+    if (s > 1) {
+      pl.splits = s;
+      pl.slabs_per_split = sps;
+      pl.ws_bytes = kCtrBytes + static_cast<size_t>(s) * tiles * pl.cfg.bm * pl.cfg.bn * sizeof(float);
+    }
+  }
+  *out = pl;
+  return DG_SUCCESS;
+}
+
+// Fills the tile grid of p and launches.  p.splits / p.slabs_per_split / p.ws /
+// p.ctr are set by the caller (dense split-K) or left at one split.
 template <int MODE>
 dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, bool e8m0, int groups_for_tiles,
                  hipStream_t stream) {
   p.tiles_m = cdiv(p.m, cfg.bm);
   p.tiles_n = cdiv(p.n, cfg.bn);
-  p.splits = 1;
-  p.slabs_per_split = p.k / 128;
-  p.ws = nullptr;
-  p.ldw = 0;
+  if (p.splits < 1) {
+    p.splits = 1;
+    p.slabs_per_split = p.k / 128;
+  }
   int cus = 0;
   dg_status st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
   const int slots = cus * cfg.per_cu;
-  bool split = false;
-  std::unique_lock<std::mutex> ws_lock;  // held until the split launches are enqueued
-  if (MODE == dg::MODE_DENSE && (cfg.id == TILE_SK_128x64 || cfg.id == TILE_SK_64x128) && p.k >= 128 * 8) {
-    int sps = 0;
-    int s = choose_splits(p.tiles_m * p.tiles_n, p.k / 128, slots, &sps);
-    if (g_force_splits > 0) {  // tuning knob: DG_FORCE_SPLITS
-      const int kb = p.k / 128;
-      sps = cdiv(kb, g_force_splits < kb ? g_force_splits : kb);
-      s = cdiv(kb, sps);
-    }
-    if (s > 1) {
-      split = true;
-      p.splits = s;
-      p.slabs_per_split = sps;
-      p.ldw = (p.n + 3) / 4 * 4;
-      st = get_workspace(static_cast<size_t>(s) * p.m * p.ldw * sizeof(float), stream, &p.ws, ws_lock);
-      if (st != DG_SUCCESS) return st;
-    }
-  }
   p.num_tiles = p.tiles_m * p.tiles_n * groups_for_tiles * p.splits;
   if (p.num_tiles <= 0) return DG_SUCCESS;
   const int grid = p.num_tiles < slots ? p.num_tiles : slots;
-  KernelFn fn = pick_kernel<MODE>(cfg, Epi{split, t == DG_DTYPE_BF16, has_c, e8m0});
+  KernelFn fn = pick_kernel<MODE>(cfg, Epi{t == DG_DTYPE_BF16, has_c, e8m0});
   if (g_print_configs)
     std::fprintf(stderr,
                  "dg: %s%s m=%d n=%d k=%d groups=%d -> BM=%d BN=%d waves=%dx%d stages=%d splits=%d (x%d slabs) "
@@ -292,14 +261,6 @@ dg_status launch(dg::Params& p, const Cfg& cfg, dg_dtype t, bool has_c, bool e8m
   hipLaunchKernelGGL(fn, dim3(grid), dim3(cfg.wm * cfg.wn * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
-  if (split) {
-    const int64_t vecs = static_cast<int64_t>(p.m) * ((p.n + 3) / 4);
-    const int64_t want = (vecs + 255) / 256;
-    const int rgrid = static_cast<int>(want < cus * 8 ? want : cus * 8);
-    hipLaunchKernelGGL(pick_reduce(t, has_c), dim3(rgrid), dim3(256), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e);
-  }
   return DG_SUCCESS;
 }
 
@@ -327,7 +288,7 @@ inline int64_t sfa_rows(int k, bool e8m0) { return sfb_row(k, e8m0); }
 
 dg_status dense_impl(const void* a, int64_t lda, const void* sfa, int64_t ld_sfa, const void* b, int64_t ldb,
                      const void* sfb, const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype, int m,
-                     int n, int k, bool e8m0, hipStream_t stream) {
+                     int n, int k, bool e8m0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m, n, k);
   if (st != DG_SUCCESS) return st;
   const int64_t es = dtype_size(d_dtype);
@@ -335,6 +296,14 @@ dg_status dense_impl(const void* a, int64_t lda, const void* sfa, int64_t ld_sfa
   if (ldd < n || (ldd * es) % 16 != 0) return DG_ERROR_INVALID_VALUE;
   if (c != nullptr && (!aligned(c, 16) || ldc < n || (ldc * es) % 16 != 0)) return DG_ERROR_INVALID_VALUE;
   if (m == 0 || n == 0) return DG_SUCCESS;
+  if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
+    return DG_ERROR_NOT_SUPPORTED;
+  DensePlan pl{};
+  st = plan_dense(m, n, k, &pl);
+  if (st != DG_SUCCESS) return st;
+  if (pl.ws_bytes > 0 &&
+      (workspace == nullptr || !aligned(workspace, kWorkspaceAlign) || workspace_bytes < pl.ws_bytes))
+    return DG_ERROR_WORKSPACE;
 
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
@@ -353,13 +322,13 @@ dg_status dense_impl(const void* a, int64_t lda, const void* sfa, int64_t ld_sfa
   p.n = n;
   p.k = k;
   p.num_groups = 1;
-  if (static_cast<int64_t>(lda) * 256 >= (1ll << 31) || static_cast<int64_t>(ldb) * 256 >= (1ll << 31))
-    return DG_ERROR_NOT_SUPPORTED;
-  int cus = 0;
-  st = usable_cus(&cus);
-  if (st != DG_SUCCESS) return st;
-  const Cfg cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? choose_wide(cdiv(m, 256), n, cus) : kCfg128);
-  return launch<dg::MODE_DENSE>(p, cfg, d_dtype, c != nullptr, e8m0, 1, stream);
+  p.splits = pl.splits;
+  p.slabs_per_split = pl.slabs_per_split;
+  if (pl.ws_bytes > 0) {
+    p.ctr = static_cast<uint32_t*>(workspace);
+    p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kCtrBytes);
+  }
+  return launch<dg::MODE_DENSE>(p, pl.cfg, d_dtype, c != nullptr, e8m0, 1, stream);
 }
 
 dg_status contiguous_impl(const void* a, const void* sfa, int64_t ld_sfa, const void* b, const void* sfb, void* d,
@@ -407,7 +376,7 @@ dg_status contiguous_impl(const void* a, const void* sfa, int64_t ld_sfa, const 
   const int64_t slots = static_cast<int64_t>(cus) * cfg.per_cu;
   const int64_t tiles = static_cast<int64_t>(cdiv(m_total, 256)) * col_tiles;
   const int64_t rounds = tiles / slots, rem = tiles % slots;
-  if (g_tail_split && cfg.bm == 256 && rounds >= 1 && rem > 0 && 2 * rem <= slots) {
+  if (cfg.bm == 256 && rounds >= 1 && rem > 0 && 2 * rem <= slots) {
     const int main_rows = static_cast<int>(rounds * slots / col_tiles) * 256;
     const int tail_rows = m_total - main_rows;
     const int64_t tail_tiles = static_cast<int64_t>(cdiv(tail_rows, 128)) * cdiv(n, 128);
@@ -525,8 +494,17 @@ extern "C" {
 
 dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
                          int64_t ldb, const float* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
-                         dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
-  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, false, stream);
+                         dg_dtype d_dtype, int m, int n, int k, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, false, workspace,
+                    workspace_bytes, stream);
+}
+
+size_t dg_get_workspace_size(int m, int n, int k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  DensePlan pl{};
+  if (plan_dense(m, n, k, &pl) != DG_SUCCESS) return 0;
+  return pl.ws_bytes;
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
@@ -546,8 +524,10 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, int64
 
 dg_status dg_fp8_gemm_nt_ue8m0(const void* a, int64_t lda, const int32_t* sfa, int64_t ld_sfa, const void* b,
                                int64_t ldb, const int32_t* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
-                               dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
-  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, true, stream);
+                               dg_dtype d_dtype, int m, int n, int k, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, true, workspace,
+                    workspace_bytes, stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t* sfa, int64_t ld_sfa,
@@ -580,8 +560,9 @@ dg_status dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const int32_t
 
 dg_status dg_wgrad_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
                                int64_t ldb, const float* sfb, float* d, int64_t ldd, int m, int n, int k,
-                               hipStream_t stream) {
-  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, d, ldd, d, ldd, DG_DTYPE_FP32, m, n, k, false, stream);
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, d, ldd, d, ldd, DG_DTYPE_FP32, m, n, k, false, workspace,
+                    workspace_bytes, stream);
 }
 
 dg_status dg_k_grouped_wgrad_fp8_gemm_nt(const void* a, const float* sfa, int64_t ld_sfa, const void* b,
@@ -609,19 +590,20 @@ dg_status dg_set_num_cus(int num_cus) {
 
 int dg_get_num_cus(void) {
   read_env();
-  return g_num_cus.load();
+  const int cap = g_num_cus.load();
+  int dev = 0, total = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&total, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || total <= 0) {
+    (void)hipGetLastError();
+    return cap;  // no device: the cap (0 = uncapped)
+  }
+  return (cap > 0 && cap < total) ? cap : total;
 }
 
-dg_status dg_set_tile_n(int tile_n) {
+dg_status dg_internal_set_tile_n(int tile_n) {
   if (tile_n != 0 && tile_n != 256 && tile_n != 224 && tile_n != 160) return DG_ERROR_INVALID_VALUE;
-  read_env();
   g_tile_n.store(tile_n);
   return DG_SUCCESS;
-}
-
-int dg_get_tile_n(void) {
-  read_env();
-  return g_tile_n.load();
 }
 
 const char* dg_status_string(dg_status s) {
@@ -630,7 +612,9 @@ const char* dg_status_string(dg_status s) {
     case DG_ERROR_INVALID_VALUE: return "DG_ERROR_INVALID_VALUE: invalid argument (pointer, alignment, stride, size or dtype)";
     case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED: shape not supported (K % 128 != 0 or contiguous M % 128 != 0)";
     case DG_ERROR_LAUNCH_FAILED: return "DG_ERROR_LAUNCH_FAILED: a HIP call failed";
-    case DG_ERROR_OUT_OF_MEMORY: return "DG_ERROR_OUT_OF_MEMORY: workspace allocation failed";
+    case DG_ERROR_WORKSPACE:
+      return "DG_ERROR_WORKSPACE: the split-K workspace is missing, not 256-byte aligned or smaller than "
+             "dg_get_workspace_size(m, n, k)";
   }
   return "DG_UNKNOWN_STATUS";
 }

@@ -75,11 +75,14 @@ struct Params {
   int m, n, k, num_groups;
   int tiles_m, tiles_n, num_tiles;
   // split-K (dense only): K slabs are divided into `splits` ranges of
-  // `slabs_per_split`; each range writes an FP32 partial tile to
-  // ws[split][m][n] (row stride ldw floats) and a second kernel reduces them.
+  // `slabs_per_split`, one work unit each.  Every unit writes its FP32
+  // partial tile to ws (unit (split s, tile t) at ws + (s * tiles + t) * BM * BN,
+  // in fragment order) and counts itself in ctr[t]; the unit that brings the
+  // count to `splits` adds the partials in split order, writes D and resets
+  // ctr[t] to zero.  ctr must be zero when the kernel starts.
   int splits, slabs_per_split;
   float* ws;
-  int64_t ldw;
+  uint32_t* ctr;
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -112,10 +115,31 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t v) {
   return v <= 0 ? 0u : (v >= 0xffffffffll ? 0xffffffffu : (uint32_t)v);
 }
 
-// 16 bytes per lane from global (descriptor + per-lane byte offset) into LDS
-// at lds_base + 16 * lane.
-__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, voff, 0, 0, 0);
+// BYTES (16 or 4) per lane from global (descriptor + per-lane byte offset)
+// into LDS at lds_base + BYTES * lane.  The kernels wait for these loads
+// with their own counted s_waitcnt.  OPAQUE issues the instruction from
+// inline asm, so that the compiler does not track it: the compiler treats a
+// tracked direct load as a pending write of LDS and, in kernels that also
+// load into registers (the split-K reduction), makes the following LDS reads
+// wait for every load in flight (s_waitcnt vmcnt(0)), which drains the
+// staging pipeline.  The instruction writes no register, so nothing the
+// compiler allocates can be overwritten by it late.
+template <int BYTES, bool OPAQUE>
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+  if constexpr (OPAQUE) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)lds_base;
+    if constexpr (BYTES == 16)
+      asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(lds)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(lds)
+                   : "memory", "m0");
+  } else if constexpr (BYTES == 16) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, voff, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 4, voff, 0, 0, 0);
+  }
 }
 
 // v_mfma_f32_16x16x128_f8f6f4, both operands E4M3 (format code 0), no block
@@ -312,7 +336,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   // belong to different groups takes one pass per group.
   struct Unit {
     int tile, pass, passes;  // tile < 0: no unit
-    int g, g0, g1, m0, n0, row_end, kb_begin, kb_end, split;
+    int g, g0, g1, m0, n0, row_end, kb_begin, kb_end, split, tmn;  // tmn: output tile within the group
   };
   // The unit (tile, pass), or the first valid one at or after it in this
   // workgroup's tile sequence.
@@ -371,6 +395,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       u.kb_begin = kb_begin;
       u.kb_end = kb_end;
       u.split = split;
+      u.tmn = t;
       break;
     }
     return u;
@@ -436,19 +461,19 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
     uint8_t* base = lds + stage * STAGE;
     if (idx < A_LOADS) {
       if (EVEN_LOADS || wave * A_LOADS + idx < A_TOTAL)
-        load_to_lds16(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
+        load_to_lds<16, SPLIT>(r.ra, base + (wave * A_LOADS + idx) * 1024, a_off[idx]);
     } else {
       if (EVEN_LOADS || wave * B_LOADS + idx - A_LOADS < B_TOTAL)
-        load_to_lds16(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
+        load_to_lds<16, SPLIT>(r.rb, base + A_BYTES + (wave * B_LOADS + idx - A_LOADS) * 1024, b_off[idx - A_LOADS]);
     }
     if (idx == 0) {
       const int q = E8M0 ? (r.kb >> 2) : r.kb;  // scale row (A) / column (B) of the slab
       if (wave == 0 && lane < SFA_LANES)
-        load_to_lds16(make_rsrc(sr.SFA + (int64_t)q * p.ld_sfa, r.live ? clamp_bytes(sr.a_rows * 4) : 0u),
-                      base + A_BYTES + B_BYTES, lane * 16);
+        load_to_lds<16, SPLIT>(make_rsrc(sr.SFA + (int64_t)q * p.ld_sfa, r.live ? clamp_bytes(sr.a_rows * 4) : 0u),
+                               base + A_BYTES + B_BYTES, lane * 16);
       if (wave == NW - 1 && lane < SFB_SLOTS)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(sr.SFB + q, r.live ? clamp_bytes((int64_t)sfb_bytes - 4 * q) : 0u),
-                                                 (lds_ptr_t)(base + SFB_OFF), 4, sr.sfb_off, 0, 0, 0);
+        load_to_lds<4, SPLIT>(make_rsrc(sr.SFB + q, r.live ? clamp_bytes((int64_t)sfb_bytes - 4 * q) : 0u),
+                              base + SFB_OFF, sr.sfb_off);
     }
   };
   auto issue_slab = [&](const Src& sr, int kb, int stage, bool live) {
@@ -474,7 +499,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   // measured 1 % slower on full 256-row tiles.
   constexpr bool XPRE = STAGES == 2;
   // BF16 output: paired 16-byte stores (see the epilogue)
-  constexpr bool PAIRED_STORES = BF16_OUT && !SPLIT;
+  constexpr bool PAIRED_STORES = BF16_OUT;
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   Unit u = find_unit(vb, 0), nx;
@@ -690,79 +715,145 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         asm volatile("" ::: "memory");  // the prefetch precedes every store below
       }
 
-      if (wave_live) {
-        if (SPLIT) {
-          // FP32 partial of this K range; the reduce kernel adds the ranges in order.
-          float* W = p.ws + (int64_t)u.split * p.m * p.ldw;
+      // Split K: publish this unit's partial and count it; only the unit that
+      // completes its tile goes on to the epilogue, with the sum of all partials.
+      bool epilogue = true;
+      if constexpr (SPLIT) {
+        if (p.splits > 1) {
+          __shared__ int s_last;
+          // Partials are stored and loaded with device-scope cache policy (sc1):
+          // the stores write through to the device's point of coherence and the
+          // loads read from it, so the units of one tile may run on different
+          // XCDs (whose L2 caches are not coherent with each other) and no L2
+          // write-back or invalidation is needed.  A unit's partial is complete
+          // at that point once its stores have been acknowledged (vmcnt 0).
+          constexpr int SC1 = 16;  // cache-policy bit of device-scope accesses
+          constexpr int64_t TILE_ELEMS = (int64_t)BM * BN;
+          const uint32_t loff = (uint32_t)(wave * FM * FN * 64 + lane) * 16;
+          auto unit_rsrc = [&](int s) {
+            return make_rsrc(p.ws + ((int64_t)s * tiles_mn + u.tmn) * TILE_ELEMS, (uint32_t)(TILE_ELEMS * 4));
+          };
+          if (wave_live) {
+            const auto rw = unit_rsrc(u.split);
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int gm = wrow0 + i * 16 + r16;
-            if (gm >= p.m) continue;
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[i][j]), rw,
+                                                       loff + (i * FN + j) * 1024, 0, SC1);
+          }
+          wait_vmcnt<0>();
+          __syncthreads();  // every wave's partial has reached the point of coherence
+          if (tid == 0) {
+            const uint32_t arrived =
+                __hip_atomic_fetch_add(p.ctr + u.tmn, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+            const int last = arrived >= (uint32_t)p.splits;
+            if (last) __hip_atomic_store(p.ctr + u.tmn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+          }
+          __syncthreads();
+          epilogue = s_last != 0;
+          if (epilogue && wave_live) {
+            // acc = partial 0 + partial 1 + ... in split order (this unit's own
+            // partial from registers); the next partial's loads are issued
+            // before the current one is added.
+            f32x4 sum[FM][FN], nxt[FM][FN];
+            auto fetch = [&](int s) {
+              if (s == u.split) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                  for (int j = 0; j < FN; ++j) nxt[i][j] = acc[i][j];
+              } else {
+                const auto rs = unit_rsrc(s);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                  for (int j = 0; j < FN; ++j)
+                    nxt[i][j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, loff + (i * FN + j) * 1024, 0, SC1));
+              }
+            };
+            fetch(0);
+            for (int s = 0; s < p.splits; ++s) {
+              f32x4 cur[FM][FN];
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) cur[i][j] = nxt[i][j];
+              if (s + 1 < p.splits) fetch(s + 1);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) sum[i][j] = s == 0 ? cur[i][j] : sum[i][j] + cur[i][j];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) acc[i][j] = sum[i][j];
+          }
+          wait_vmcnt<0>();
+        }
+      }
+
+      if (wave_live && epilogue) {
+        // Epilogue: D = C + acc, masked stores.  (The empty asm makes the row
+        // index opaque, so the row addresses are computed here instead of being
+        // hoisted above the K loop, where registers are scarce.)
+        int row0 = wrow0 + r16;
+        asm volatile("" : "+v"(row0));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int gm = row0 + i * 16;
+          bool row_ok = gm < row_end;
+          if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
+          const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
+          const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
+          if constexpr (PAIRED_STORES) {
+            // Adjacent column fragments j, j+1 in BF16: one permlane16 swap per
+            // word pair leaves each lane 8 consecutive columns of its row
+            // (16-lane row q4 even: fragment j, odd: j+1; columns 8 * (q4 / 2) ..),
+            // so a row's 64 bytes go out as four 16-byte stores instead of eight
+            // of 8 bytes.  The swap partners share r16, hence the row and its
+            // row_ok; the swaps run before the row test, on the whole wave.
+#pragma unroll
+            for (int j = 0; j + 1 < FN; j += 2) {
+              if (HAS_C && row_ok) {  // C in the MFMA layout: this lane's row, columns 4 * q4 ..
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const int gc = n0 + wn * TN + (j + h) * 16 + 4 * q4;
+                  if (gc < p.n) add_c_bf16(p, crow, gc, acc[i][j + h]);
+                }
+              }
+              const auto s0 = __builtin_amdgcn_permlane16_swap(bf16x2_rne_bits(acc[i][j][0], acc[i][j][1]),
+                                                               bf16x2_rne_bits(acc[i][j + 1][0], acc[i][j + 1][1]),
+                                                               false, false);
+              const auto s1 = __builtin_amdgcn_permlane16_swap(bf16x2_rne_bits(acc[i][j][2], acc[i][j][3]),
+                                                               bf16x2_rne_bits(acc[i][j + 1][2], acc[i][j + 1][3]),
+                                                               false, false);
+              const int gn = n0 + wn * TN + (j + (q4 & 1)) * 16 + 8 * (q4 >> 1);
+              if (!row_ok || gn >= p.n) continue;
+              uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
+              const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
+              if (gn + 8 <= p.n) {
+                *reinterpret_cast<uint4*>(D) = make_uint4(w[0], w[1], w[2], w[3]);
+              } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                  if (gn + c < p.n) D[c] = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
+              }
+            }
+            if constexpr (FN % 2 == 1) {
+              const int gn = n0 + wn * TN + (FN - 1) * 16 + 4 * q4;
+              if (row_ok && gn < p.n) store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][FN - 1]);
+            }
+          } else {
+            if (!row_ok) continue;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
               const int gn = n0 + wn * TN + j * 16 + 4 * q4;
-              if (gn < p.n) *reinterpret_cast<f32x4*>(W + (int64_t)gm * p.ldw + gn) = acc[i][j];
-            }
-          }
-        } else {
-          // Epilogue: D = C + acc, masked stores.  (The empty asm makes the row
-          // index opaque, so the row addresses are computed here instead of being
-          // hoisted above the K loop, where registers are scarce.)
-          int row0 = wrow0 + r16;
-          asm volatile("" : "+v"(row0));
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int gm = row0 + i * 16;
-            bool row_ok = gm < row_end;
-            if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
-            const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
-            const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
-            if constexpr (PAIRED_STORES) {
-              // Adjacent column fragments j, j+1 in BF16: one permlane16 swap per
-              // word pair leaves each lane 8 consecutive columns of its row
-              // (16-lane row q4 even: fragment j, odd: j+1; columns 8 * (q4 / 2) ..),
-              // so a row's 64 bytes go out as four 16-byte stores instead of eight
-              // of 8 bytes.  The swap partners share r16, hence the row and its
-              // row_ok; the swaps run before the row test, on the whole wave.
-#pragma unroll
-              for (int j = 0; j + 1 < FN; j += 2) {
-                if (HAS_C && row_ok) {  // C in the MFMA layout: this lane's row, columns 4 * q4 ..
-#pragma unroll
-                  for (int h = 0; h < 2; ++h) {
-                    const int gc = n0 + wn * TN + (j + h) * 16 + 4 * q4;
-                    if (gc < p.n) add_c_bf16(p, crow, gc, acc[i][j + h]);
-                  }
-                }
-                const auto s0 = __builtin_amdgcn_permlane16_swap(bf16x2_rne_bits(acc[i][j][0], acc[i][j][1]),
-                                                                 bf16x2_rne_bits(acc[i][j + 1][0], acc[i][j + 1][1]),
-                                                                 false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(bf16x2_rne_bits(acc[i][j][2], acc[i][j][3]),
-                                                                 bf16x2_rne_bits(acc[i][j + 1][2], acc[i][j + 1][3]),
-                                                                 false, false);
-                const int gn = n0 + wn * TN + (j + (q4 & 1)) * 16 + 8 * (q4 >> 1);
-                if (!row_ok || gn >= p.n) continue;
-                uint16_t* D = reinterpret_cast<uint16_t*>(p.d) + drow + gn;
-                const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
-                if (gn + 8 <= p.n) {
-                  *reinterpret_cast<uint4*>(D) = make_uint4(w[0], w[1], w[2], w[3]);
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 8; ++c)
-                    if (gn + c < p.n) D[c] = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
-                }
-              }
-              if constexpr (FN % 2 == 1) {
-                const int gn = n0 + wn * TN + (FN - 1) * 16 + 4 * q4;
-                if (row_ok && gn < p.n) store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][FN - 1]);
-              }
-            } else {
-              if (!row_ok) continue;
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int gn = n0 + wn * TN + j * 16 + 4 * q4;
-                if (gn >= p.n) continue;
-                store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
-              }
+              if (gn >= p.n) continue;
+              store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
             }
           }
         }
@@ -771,34 +862,6 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
     }
     u = nx;
     pre = pre_next;
-  }
-}
-
-// Split-K reduction: D = C + sum over splits (in split order) of the FP32
-// partials ws[s][m][n]; one thread per 4 consecutive columns of a row.  The
-// partials are loaded eight at a time before they are added (in order), so
-// their latencies overlap instead of adding up.
-template <bool BF16_OUT, bool HAS_C>
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const Params p) {
-  constexpr int BATCH = 8;
-  const int vec_per_row = (p.n + 3) >> 2;
-  const int64_t total = (int64_t)p.m * vec_per_row;
-  const int64_t split_stride = (int64_t)p.m * p.ldw;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int gm = (int)(idx / vec_per_row);
-    const int gn = (int)(idx - (int64_t)gm * vec_per_row) * 4;
-    const float* W = p.ws + (int64_t)gm * p.ldw + gn;
-    f32x4 v = *reinterpret_cast<const f32x4*>(W);
-    for (int s = 1; s < p.splits; s += BATCH) {
-      f32x4 t[BATCH];
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        if (s + j < p.splits) t[j] = *reinterpret_cast<const f32x4*>(W + (s + j) * split_stride);
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        if (s + j < p.splits) v += t[j];
-    }
-    store_out<BF16_OUT, HAS_C>(p, (int64_t)gm * p.ldc, gn, (int64_t)gm * p.ldd, v);
   }
 }
 

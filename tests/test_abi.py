@@ -33,8 +33,24 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for want in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
                  "dg_get_mk_alignment_for_contiguous_layout", "dg_get_sf_aligned_size", "dg_set_num_cus",
-                 "dg_get_num_cus", "dg_status_string"):
+                 "dg_get_num_cus", "dg_status_string", "dg_get_workspace_size"):
         assert want in names
+    # the configuration surface is the CU cap and DG_PRINT_CONFIGS; tile widths are not part of it
+    assert not [n for n in names if "tile_n" in n or "internal" in n]
+
+
+def test_workspace_size_of_invalid_sizes_is_zero(lib):
+    for m, n, k in ((0, 256, 512), (64, 0, 512), (64, 256, 0), (64, 256, 500), (-1, 256, 512)):
+        assert lib.dg_get_workspace_size(m, n, k) == 0
+
+
+def test_library_allocates_nothing():
+    """The library source makes no allocation, free or host synchronisation."""
+    src = os.path.join(ROOT, "moe_grouped_gemm_tiles_amd", "csrc")
+    for f in os.listdir(src):
+        text = re.sub(r"//[^\n]*", "", open(os.path.join(src, f)).read())
+        for call in ("hipMalloc", "hipFree", "hipStreamSynchronize", "hipDeviceSynchronize", "hipHostMalloc"):
+            assert call not in text, (f, call)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,9 +67,9 @@ def test_utilities(lib):
     assert lib.dg_set_num_cus(64) == 0 and lib.dg_get_num_cus() == 64
     assert lib.dg_set_num_cus(0) == 0 and lib.dg_get_num_cus() == 0
     for bad in (-1, 1, 128, 192, 512):
-        assert lib.dg_set_tile_n(bad) == INVALID
+        assert lib.dg_internal_set_tile_n(bad) == INVALID
     for w in (256, 224, 160, 0):
-        assert lib.dg_set_tile_n(w) == 0 and lib.dg_get_tile_n() == w
+        assert lib.dg_internal_set_tile_n(w) == 0
     for s in range(5):
         assert lib.dg_status_string(s)
     assert lib.dg_status_string(99) == b"DG_UNKNOWN_STATUS"
@@ -69,7 +85,7 @@ def _dense(lib, **kw):
     args.update(kw)
     return lib.dg_fp8_gemm_nt(args["a"], args["lda"], args["sfa"], args["ld_sfa"], args["b"], args["ldb"],
                               args["sfb"], args["c"], args["ldc"], args["d"], args["ldd"], args["dt"],
-                              args["m"], args["n"], args["k"], None)
+                              args["m"], args["n"], args["k"], None, 0, None)
 
 
 def test_dense_validation(lib):
@@ -151,7 +167,7 @@ def test_header_declares_next_entry_points():
 
 def test_ue8m0_validation(lib):
     f = lib.dg_fp8_gemm_nt_ue8m0
-    ok = (P, 512, P, 128, P, 512, P, None, 0, P, 256, 0, 128, 256, 512, None)
+    ok = (P, 512, P, 128, P, 512, P, None, 0, P, 256, 0, 128, 256, 512, None, 0, None)
     bad_ld = list(ok)
     bad_ld[3] = 130  # ld_sfa not a multiple of 4 words
     assert f(*bad_ld) == INVALID
@@ -185,8 +201,8 @@ def test_k_grouped_and_wgrad_validation(lib):
     assert _kg(lib, ld_sfa=100) == INVALID
     assert _kg(lib, m=0) == 0 and _kg(lib, g=0) == 0
     w = lib.dg_wgrad_fp8_gemm_nt
-    assert w(P, 512, P, 128, P, 512, P, P, 100, 128, 256, 512, None) == INVALID  # ldd < n
-    assert w(P, 512, P, 128, P, 512, P, P, 256, 0, 256, 512, None) == 0
+    assert w(P, 512, P, 128, P, 512, P, P, 100, 128, 256, 512, None, 0, None) == INVALID  # ldd < n
+    assert w(P, 512, P, 128, P, 512, P, P, 256, 0, 256, 512, None, 0, None) == 0
     kw = lib.dg_k_grouped_wgrad_fp8_gemm_nt
     assert kw(P, P, 256, P, P, P, None, 4, 256, 256, 1024, None) == INVALID  # no ks
     ku = lib.dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0

@@ -1,10 +1,10 @@
-"""HIP-graph capture of library calls (the benchmark times graph replays).
+"""HIP-graph capture of library calls.
 
-The calls are captured on one stream after an eager run on that stream (which
-creates any split-K workspace, so nothing is allocated during capture).  The
-graph is replayed several times with eager work and synchronisations between
-replays, and every replay must reproduce the eager outputs bit for bit,
-including the rows the library must leave unwritten.
+The library allocates nothing and never synchronises, so every entry point can
+be captured, also as the first call of its shape.  Graphs are replayed several
+times with eager work and synchronisations between replays, and every replay
+must reproduce the eager outputs bit for bit, including the rows the library
+must leave unwritten.
 """
 
 import numpy as np
@@ -42,7 +42,9 @@ def _calls():
         dt = torch.bfloat16 if x["out_dtype"] == "bf16" else torch.float32
         d = torch.empty(x["m"], x["n"], dtype=dt, device="cuda:0")
         c = to_dev(x["c"]).to(dt) if x["c"] is not None else None
-        out.append((name, (lambda a=a, b=b, sfa=sfa, sfb=sfb, d=d, c=c: dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c)), d))
+        ws = dg.alloc_workspace(x["m"], x["n"], x["k"])
+        out.append((name, (lambda a=a, b=b, sfa=sfa, sfb=sfb, d=d, c=c, ws=ws:
+                           dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c, workspace=ws)), d))
     x = gen_contiguous(3, 384, 512, seed=94, m_sizes=[130, 0, 200])
     d = torch.empty(x["m_total"], 384, dtype=torch.bfloat16, device="cuda:0")
     args = ((fp8_dev(x["a"]), to_dev(x["sfa"])), (fp8_dev(x["b"]), to_dev(x["sfb"])), d, to_dev(x["m_indices"]))
@@ -101,3 +103,46 @@ def test_graph_replays_match_eager():
         for (name, _, d), want in zip(calls, ref):
             assert torch.equal(_bits(d), want), f"replay {r}: {name} differs from the eager result"
         note(f"replay {r}: all {len(calls)} outputs bit-identical to eager")
+
+
+def test_split_k_captured_first_and_replayed_on_another_stream():
+    """Skinny (split-K) calls captured with no eager call of their shape before, one with
+    a caller workspace and one with the per-call workspace the binding takes from torch
+    (allocated and cleared inside the capture); replays alternate between the capture
+    stream and a second stream and must equal eager calls made afterwards."""
+    xs = [gen_dense(64, 2112, 7168, seed=190), gen_dense(100, 1040, 4096, seed=191, with_c=True),
+          gen_dense(128, 24576, 1536, seed=192)]
+    dev = []
+    for x in xs:
+        c = to_dev(x["c"]).to(torch.bfloat16) if x["c"] is not None else None
+        dev.append((fp8_dev(x["a"]), to_dev(x["sfa"]), fp8_dev(x["b"]), to_dev(x["sfb"]), c,
+                    torch.empty(x["m"], x["n"], dtype=torch.bfloat16, device="cuda:0")))
+    ws0 = dg.alloc_workspace(64, 2112, 7168)
+    ws2 = dg.alloc_workspace(128, 24576, 1536)
+    wss = [ws0, None, ws2]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s1):
+        for (a, sfa, b, sfb, c, d), ws in zip(dev, wss):
+            dg.fp8_gemm_nt((a, sfa), (b, sfb), d, c, workspace=ws)
+    torch.cuda.synchronize()
+    want = []
+    for a, sfa, b, sfb, c, d in dev:  # eager, each with a fresh workspace
+        e = torch.empty_like(d)
+        dg.fp8_gemm_nt((a, sfa), (b, sfb), e, c)
+        want.append(e)
+    torch.cuda.synchronize()
+    want = [_bits(e) for e in want]
+    scratch = torch.randn(1 << 20, device="cuda:0")
+    for r in range(6):
+        for *_, d in dev:
+            _sentinel_fill(d)
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s2 if r % 2 else s1):
+            g.replay()
+        torch.cuda.synchronize()
+        for i, (*_, d) in enumerate(dev):
+            assert torch.equal(_bits(d), want[i]), f"replay {r}: call {i} differs from the eager result"
+        note(f"replay {r} on stream {2 if r % 2 else 1}: split-K outputs bit-identical to eager")

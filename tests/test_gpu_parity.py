@@ -253,7 +253,7 @@ def test_contiguous_ragged_last_round_split(fmt):
 
 @pytest.mark.parametrize("m,out", [(48, "fp32"), (128, "bf16"), (100, "fp32")])
 def test_dense_split_k_with_c(m, out):
-    """Skinny M takes the split-K path (FP32 partials + ordered reduction); C is added once."""
+    """Skinny M takes the split-K path (FP32 partials, ordered in-kernel reduction); C is added once."""
     x = gen_dense(m, 520, 2048, seed=60 + m, with_c=True, out_dtype=out)
     _check_dense(x, run_dense(x, ld_d=528), f"split-K + C M={m} {out}")
 
@@ -267,9 +267,9 @@ def test_split_k_determinism_and_sentinel_columns():
 
 
 def test_split_k_threads_sharing_a_stream():
-    """Two host threads issue skinny (split-K) calls of different shapes on one fresh
-    stream: each call's GEMM and reduction use the stream's workspace as one unit (the
-    workspace grows on the way), so every output equals the single-threaded result."""
+    """Two host threads issue skinny (split-K) calls of different shapes on one stream,
+    each call with the workspace the binding takes from torch's allocator: every output
+    equals the single-threaded result."""
     import threading
 
     xs = [gen_dense(64, 2112, 7168, seed=70), gen_dense(100, 1040, 4096, seed=71)]

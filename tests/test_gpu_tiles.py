@@ -1,5 +1,5 @@
 """GPU parity of every width of the 256-row tiles (256, 224 and 160 columns,
-forced with ``set_tile_n``) against the FP64 CPU oracle, in every GEMM mode.
+forced with ``_set_tile_n_for_tests``) against the FP64 CPU oracle, in every GEMM mode.
 
 The 224- and 160-column tiles do not align with the 128-column scale blocks
 of B, so a wave's fragments can straddle two blocks and take their B scale
@@ -29,10 +29,10 @@ if torch.cuda.is_available():  # pragma: no cover - GPU only
 
 @pytest.fixture
 def tile_n(request):
-    dg.set_tile_n(request.param)
+    dg._set_tile_n_for_tests(request.param)
     note(f"tile width {request.param}")
     yield request.param
-    dg.set_tile_n(0)
+    dg._set_tile_n_for_tests(0)
 
 
 def _one_hot(rng, m, n, k):
@@ -127,10 +127,10 @@ def test_automatic_width_matches_forced(m, n, k):
     same = []
     try:
         for w in WIDTHS:
-            dg.set_tile_n(w)
+            dg._set_tile_n_for_tests(w)
             same.append(np.array_equal(raw_bits(run_dense(x)), auto))
     finally:
-        dg.set_tile_n(0)
+        dg._set_tile_n_for_tests(0)
     assert any(same)
     # checked against the oracle on sampled rows and columns
     rng = np.random.default_rng(96)

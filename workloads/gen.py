@@ -323,7 +323,7 @@ DENSE_SWEEP_NK = [(2112, 7168), (24576, 1536), (7168, 16384), (4096, 7168), (716
 DENSE_SWEEP_M = [64, 128, 4096]
 DENSE_SWEEP = [(m, n, k) for m in DENSE_SWEEP_M for (n, k) in DENSE_SWEEP_NK]
 
-WORKLOAD_NAMES = ("dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc",
+WORKLOAD_NAMES = ("baseline", "dense_small", "dense_sweep", "contiguous_moe", "masked_decode", "dense_long_k_acc",
                   "dense_sweep_ue8m0", "contiguous_moe_ue8m0", "masked_decode_ue8m0", "k_grouped_wgrad",
                   "quant_moe", "mqa_logits")
 
@@ -333,6 +333,15 @@ def workload(name: str):
 
     Each descriptor is a dict with a ``gen`` callable producing the inputs.
     """
+    if name == "baseline":
+        # the five benchmark configurations in order: small dense, the dense sweep,
+        # contiguous MoE, masked decode (both shapes), long-K dense with FP32 C/D
+        out = []
+        for cfg, part in ((0, "dense_small"), (1, "dense_sweep"), (2, "contiguous_moe"), (3, "masked_decode"),
+                          (4, "dense_long_k_acc")):
+            for d in workload(part):
+                out.append(dict(d, config=cfg))
+        return out
     if name == "dense_small":
         return [dict(label="dense M=128 N=256 K=512", kind="dense", m=128, n=256, k=512,
                      gen=lambda: gen_dense(128, 256, 512, seed=0))]
