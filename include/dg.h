@@ -71,7 +71,8 @@ typedef enum {
   DG_ERROR_INVALID_VALUE = 1,  /* null/misaligned pointer, bad stride, negative size, bad enum */
   DG_ERROR_NOT_SUPPORTED = 2,  /* valid but unsupported: K % 128 != 0, contiguous M % 128 != 0 */
   DG_ERROR_LAUNCH_FAILED = 3,  /* a HIP call failed; hipGetLastError() text via dg_last_hip_error */
-  DG_ERROR_WORKSPACE = 4       /* split-K workspace NULL, misaligned or smaller than dg_get_workspace_size */
+  DG_ERROR_WORKSPACE = 4,      /* split-K workspace NULL, misaligned or smaller than dg_get_workspace_size */
+  DG_ERROR_SCRATCH_LIMIT = 5   /* dg_fp8_gemm_nt_noalloc: the call needs more than the library's fixed scratch */
 } dg_status;
 
 typedef enum { DG_DTYPE_BF16 = 0, DG_DTYPE_FP32 = 1 } dg_dtype;
@@ -100,6 +101,29 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
                          const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
                          int m, int n, int k, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/*
+ * Allocation-free form of dg_fp8_gemm_nt, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, kernels and bits as
+ * dg_fp8_gemm_nt with a workspace, but the split-K scratch is a fixed array
+ * inside the library (64 KiB of counters + 16 MiB of partial tiles on each
+ * device, held from the library's first use on that device until the process
+ * ends).  No memory is allocated or freed by the call.
+ *   - Every call on a device shares that device's scratch: calls that overlap
+ *     on one device (other streams, other host threads) RACE and may return
+ *     wrong results; order them (one stream).
+ *   - Each split call first clears the counters it uses (one small kernel on
+ *     `stream`), so a call does not depend on what the previous one left.
+ *   - A call that needs more scratch than the fixed size (more than two
+ *     units of 32 KiB per CU, never the case on a 256-CU device) ->
+ *     DG_ERROR_SCRATCH_LIMIT, nothing enqueued.
+ * Arguments, layouts and other errors as for dg_fp8_gemm_nt.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
+                                 const void* b, int64_t ldb, const float* sfb,
+                                 const void* c, int64_t ldc, void* d, int64_t ldd, dg_dtype d_dtype,
+                                 int m, int n, int k, hipStream_t stream);
 
 /*
  * Bytes of split-K workspace the dense GEMMs (dg_fp8_gemm_nt, its UE8M0 form

@@ -92,6 +92,8 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
                               _i32, _i32, _i32, _vp, _sz, _vp]),
     "dg_get_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "dg_fp8_gemm_nt_noalloc": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32,
+                                      _i32, _i32, _i32, _vp]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
                                                    _i32, _i32, _i32, _i32, _vp]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp,

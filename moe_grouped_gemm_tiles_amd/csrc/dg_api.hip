@@ -182,7 +182,10 @@ Cfg choose_wide(int64_t row_tiles, int n, int slots) {
 // the last unit of each tile reads back.  Fitted to cold timings of the
 // dense-sweep shapes with M <= 128 over forced split counts 1..32: the best
 // counts keep about one unit per CU (a second unit on a CU shares its memory
-// pipeline) and stop short of many small splits.
+// pipeline) and stop short of many small splits.  Splits that would make more
+// than two units per CU are not considered (splitting pays only while the
+// tiles leave CUs idle), which also bounds the workspace to 2 x CUs partial
+// tiles.
 int choose_splits(int tiles, int kb, int cus, int* slabs_per_split) {
   int best_s = 1, best_sps = kb;
   double best_cost = 1e300;
@@ -190,6 +193,7 @@ int choose_splits(int tiles, int kb, int cus, int* slabs_per_split) {
     const int sps = cdiv(kb, s);
     const int s_eff = cdiv(kb, sps);
     if (s_eff != s) continue;
+    if (s > 1 && static_cast<int64_t>(tiles) * s > 2ll * cus) break;
     const int rounds = cdiv(tiles * s_eff, cus);
     const double cost = static_cast<double>(rounds) * (sps + 6.0) + 0.5 * (s_eff - 1);
     if (cost < best_cost - 1e-9) {
@@ -477,6 +481,40 @@ dg_status k_grouped_impl(const void* a, const void* sfa, int64_t ld_sfa, const v
   return launch<dg::MODE_KGROUP>(p, cfg, DG_DTYPE_FP32, c != nullptr, e8m0, num_groups, stream);
 }
 
+// ---- allocation-free dense entry point ---------------------------------------
+// Split-K scratch of dg_fp8_gemm_nt_noalloc: counters then partials, the
+// largest workspace plan_dense asks for on a 256-CU device (two units per CU
+// of 32 KiB partial tiles).  Each device holds its own copy; its address comes
+// from hipGetSymbolAddress on that device (the name itself is only a host-side
+// stand-in) and is kept per device.
+constexpr size_t kScratchBytes = kCtrBytes + (size_t(16) << 20);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dg_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return DG_ERROR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_SUCCESS;
+}
+
+// Zero n counter words (a kernel, not hipMemsetAsync, so the call stays
+// capturable into a graph that is replayed many times).
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
 
 namespace dg {
@@ -498,6 +536,32 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
                          hipStream_t stream) {
   return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, false, workspace,
                     workspace_bytes, stream);
+}
+
+dg_status dg_fp8_gemm_nt_noalloc(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa, const void* b,
+                                 int64_t ldb, const float* sfb, const void* c, int64_t ldc, void* d, int64_t ldd,
+                                 dg_dtype d_dtype, int m, int n, int k, hipStream_t stream) {
+  dg_status st = check_common(a, sfa, ld_sfa, b, sfb, d, d_dtype, m, n, k);
+  if (st != DG_SUCCESS || m == 0 || n == 0) return st;
+  DensePlan pl{};
+  if (k % 128 == 0 && m > 0 && n > 0 && k > 0) {
+    st = plan_dense(m, n, k, &pl);
+    if (st != DG_SUCCESS) return st;
+  }
+  if (pl.ws_bytes > kScratchBytes) return DG_ERROR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_address(&ws);
+    if (st != DG_SUCCESS) return st;
+    // the counters of this call's tiles start at zero whatever the last call left
+    const int words = cdiv(m, pl.cfg.bm) * cdiv(n, pl.cfg.bn);  // one counter per output tile
+    const int grid = cdiv(words, 256) < 64 ? cdiv(words, 256) : 64;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint32_t*>(ws), words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return dense_impl(a, lda, sfa, ld_sfa, b, ldb, sfb, c, ldc, d, ldd, d_dtype, m, n, k, false, ws,
+                    ws != nullptr ? kScratchBytes : 0, stream);
 }
 
 size_t dg_get_workspace_size(int m, int n, int k) {
@@ -612,6 +676,9 @@ const char* dg_status_string(dg_status s) {
     case DG_ERROR_INVALID_VALUE: return "DG_ERROR_INVALID_VALUE: invalid argument (pointer, alignment, stride, size or dtype)";
     case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED: shape not supported (K % 128 != 0 or contiguous M % 128 != 0)";
     case DG_ERROR_LAUNCH_FAILED: return "DG_ERROR_LAUNCH_FAILED: a HIP call failed";
+    case DG_ERROR_SCRATCH_LIMIT:
+      return "DG_ERROR_SCRATCH_LIMIT: the call needs more split-K scratch than the allocation-free entry point "
+             "holds (16 MiB of partial tiles); use dg_fp8_gemm_nt with a workspace";
     case DG_ERROR_WORKSPACE:
       return "DG_ERROR_WORKSPACE: the split-K workspace is missing, not 256-byte aligned or smaller than "
              "dg_get_workspace_size(m, n, k)";
