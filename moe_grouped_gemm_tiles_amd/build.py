@@ -6,6 +6,12 @@ compiler for each kernel's resource usage and fails if any kernel spills to
 scratch memory (the counterpart of DeepGEMM's DG_JIT_PTXAS_CHECK switch,
 README section "Utilities", which asserts no local memory use); the usage
 table is written next to the library as ``libdg.resources.txt``.
+
+It also builds ``libdg_debug.so``: the same sources with
+``-DDG_DEBUG_LDS_BARRIERS=1``, which puts a full wait and a workgroup barrier
+after every phase of LDS traffic in the GEMM kernels.  Tests compare its
+outputs bit for bit with the normal library's (an LDS race shows up as a
+difference); it is never loaded by the package.
 """
 
 from __future__ import annotations
@@ -21,6 +27,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdg.so")
+DEBUG_LIB = os.path.join(PKG, "libdg_debug.so")
 RES = os.path.join(PKG, "libdg.resources.txt")
 ARCH = "gfx950"
 
@@ -35,9 +42,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def compile_cmd(out: str) -> list:
+def compile_cmd(out: str, debug_barriers: bool = False) -> list:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        *(["-DDG_DEBUG_LDS_BARRIERS=1"] if debug_barriers else []),
         # packed FP32 instructions stay off for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # MFMA results feed VALU promotion: keep them in VGPRs (no AGPR round trip)
@@ -69,16 +77,28 @@ def _parse_resources(stderr: str):
     return kernels
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = compile_cmd(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
-    kernels = _parse_resources(proc.stderr)
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Builds libdg.so (and, unless debug=False, libdg_debug.so, compiled at the
+    same time); returns the library path."""
+    jobs = [(LIB, RES, False)] + ([(DEBUG_LIB, None, True)] if debug else [])
+    running = []
+    for lib, res, dbg in jobs:
+        cmd = compile_cmd(lib + ".tmp", dbg)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        running.append((lib, res, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    for lib, res, proc in running:
+        out, err = proc.communicate()
+        _finish(lib, res, proc.returncode, out, err, verbose)
+    return LIB
+
+
+def _finish(lib: str, res, returncode: int, out: str, err: str, verbose: bool):
+    tmp = lib + ".tmp"
+    if returncode != 0:
+        sys.stderr.write(out + err)
+        raise RuntimeError(f"hipcc failed with exit code {returncode} building {os.path.basename(lib)}")
+    kernels = _parse_resources(err)
     lines = [f"{'kernel':<90} {'vgpr':>5} {'agpr':>5} {'sgpr':>5} {'scratch':>8} {'lds':>7} {'occ':>4}"]
     spills = []
     for kr in kernels:
@@ -87,16 +107,19 @@ def build(verbose: bool = False) -> str:
                      f"{kr.get('occupancy', -1):>4}")
         if kr.get("scratch", 0) != 0:
             spills.append(kr["name"])
-    with open(RES, "w") as f:
-        f.write("\n".join(lines) + "\n")
+    if res is not None:
+        with open(res, "w") as f:
+            f.write("\n".join(lines) + "\n")
     if spills:
         print("\n".join(lines), file=sys.stderr)
         os.unlink(tmp)
-        raise RuntimeError("kernels use scratch memory (register spills): " + ", ".join(spills))
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"{os.path.basename(lib)}: kernels use scratch memory (register spills): "
+                           + ", ".join(spills))
+    os.replace(tmp, lib)
     if verbose:
-        print("\n".join(lines))
-    return LIB
+        print(f"built {lib}")
+        if res is not None:
+            print("\n".join(lines))
 
 
 if __name__ == "__main__":

@@ -106,6 +106,24 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// LDS-race debug build (compiled with -DDG_DEBUG_LDS_BARRIERS=1): after every
+// phase of LDS traffic (the prologue's loads, each slab's part 1 and part 2,
+// the unit's epilogue) every wave waits for all of its memory operations and
+// meets a workgroup barrier.  The arithmetic is unchanged, so its results must
+// equal the normal build's bit for bit; a difference means a missing wait or
+// barrier in the normal schedule.  Called only where every wave arrives.
+#ifndef DG_DEBUG_LDS_BARRIERS
+#define DG_DEBUG_LDS_BARRIERS 0
+#endif
+__device__ __forceinline__ void debug_fence() {
+  if constexpr (DG_DEBUG_LDS_BARRIERS != 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+}
+
 // Raw buffer descriptor: loads at byte offsets >= num_bytes return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
@@ -553,6 +571,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         }
         stage_barrier();
         if (pre == 0) issue_slab(sr, kb_begin + STAGES - 1, STAGES - 1, STAGES - 1 < nkb);
+        debug_fence();
 
         const uint8_t* As0 = lds + (wm * TM + r16) * 128;
         const uint8_t* Bs0 = lds + A_BYTES + (wn * TN + r16) * 128;
@@ -655,6 +674,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             for (int idx = P2L; idx < LOADS; ++idx) issue_load(sr, pr, nxt, idx);
           }
 
+          debug_fence();
           // slab it + 1 has landed (this wave's part of it)
           wait_slab();
           stage_barrier();
@@ -689,6 +709,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           }
 #pragma unroll
           for (int idx = P2; idx < P2L; ++idx) issue_load(sr, nr, cur, idx);
+          debug_fence();
         }
         // promote the last slab's tail
         if (wave_live) {
@@ -704,6 +725,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         }
       }
       stage_barrier();  // all LDS reads of this unit are done before the next unit's loads
+      debug_fence();
 
       // next unit: its first two slabs go out before this unit's stores
       nx = next_unit(u);
@@ -859,6 +881,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         }
       }
       asm volatile("" ::: "memory");  // every store precedes the next unit's first wait
+      debug_fence();
     }
     u = nx;
     pre = pre_next;

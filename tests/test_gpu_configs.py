@@ -27,6 +27,36 @@ def _sample(rng, total, count, must=()):
     return np.array(sorted(pick))
 
 
+# Output tile sizes the dispatcher can pick: 256-row tiles of 256, 224 or 160
+# columns (the skinny and 128-row tiles divide these).
+ROW_PERIODS = (256,)
+COL_PERIODS = (256, 224, 160)
+
+
+def _cover(rng, total, periods, valid=None, must=()):
+    """Indices in [0, total) such that, for every period p, every residue mod p
+    that occurs among the (valid) indices is present at least once, each taken
+    from a randomly chosen tile; plus ``must``."""
+    pick = set(int(v) for v in must if 0 <= v < total and (valid is None or valid[v]))
+    for p in periods:
+        idx = np.arange(total)
+        for r in range(min(p, total)):
+            cand = idx[r::p]
+            if valid is not None:
+                cand = cand[valid[cand]]
+            if len(cand):
+                pick.add(int(rng.choice(cand)))
+    return np.array(sorted(pick))
+
+
+def _assert_covers(idx, total, periods, valid=None, what=""):
+    ok = np.ones(total, bool) if valid is None else valid
+    for p in periods:
+        need = set(np.nonzero(ok)[0] % p)
+        got = set(np.asarray(idx) % p)
+        assert need <= got, f"{what}: residues mod {p} not compared: {sorted(need - got)[:8]}"
+
+
 @pytest.mark.parametrize("i", range(len(DENSE_SWEEP)))
 def test_dense_sweep_full_size(i):
     m, n, k = DENSE_SWEEP[i]
@@ -35,8 +65,10 @@ def test_dense_sweep_full_size(i):
     d = run_dense(x)
     assert torch.isfinite(d.float()).all()
     rng = np.random.default_rng(1000 + i)
-    rows = _sample(rng, m, 48, must=(0, m - 1))
-    cols = _sample(rng, n, 768, must=range(n - 70, n))
+    rows = _cover(rng, m, ROW_PERIODS, must=(0, m - 1))
+    cols = _cover(rng, n, COL_PERIODS, must=range(n - 70, n))
+    _assert_covers(rows, m, ROW_PERIODS, what="rows")
+    _assert_covers(cols, n, COL_PERIODS, what="cols")
     ref = oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], rows=rows, cols=cols)
     rep = oracle.assert_close(take(d, rows, cols), ref, f"dense M={m} N={n} K={k}")
     note(f"  worst={rep['worst_ratio']:.3f} cos_dist={rep['cos_dist']:.2e} sampled={rep['n']}")
@@ -48,8 +80,10 @@ def test_dense_long_k_with_c_full_size():
     d = run_dense(x)
     assert torch.isfinite(d).all()
     rng = np.random.default_rng(44)
-    rows = _sample(rng, 8192, 24, must=(0, 8191))
-    cols = _sample(rng, 8192, 512, must=(0, 8191))
+    rows = _cover(rng, 8192, ROW_PERIODS, must=(0, 8191))
+    cols = _cover(rng, 8192, COL_PERIODS, must=(0, 8191))
+    _assert_covers(rows, 8192, ROW_PERIODS, what="rows")
+    _assert_covers(cols, 8192, COL_PERIODS, what="cols")
     ref = oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], x["c"], rows=rows, cols=cols)
     rep = oracle.assert_close(take(d, rows, cols), ref, "dense+C long K")
     note(f"  worst={rep['worst_ratio']:.3f} cos_dist={rep['cos_dist']:.2e}")
@@ -69,9 +103,10 @@ def test_contiguous_moe_full_size():
     ends = starts + x["m_sizes"] - 1
     # rows of the last 512, which a ragged last round sends to the 128x128 launch
     tail = x["m_total"] - np.array([512, 511, 384, 257, 256, 129, 1])
-    rows = _sample(rng, x["m_total"], 64, must=np.concatenate([starts, ends, tail]))
-    rows = rows[written[rows]]
-    cols = _sample(rng, 4096, 512, must=(0, 4095))
+    rows = _cover(rng, x["m_total"], ROW_PERIODS, valid=written, must=np.concatenate([starts, ends, tail]))
+    cols = _cover(rng, 4096, COL_PERIODS, must=(0, 4095))
+    _assert_covers(rows, x["m_total"], ROW_PERIODS, valid=written, what="rows")
+    _assert_covers(cols, 4096, COL_PERIODS, what="cols")
     ref, w = oracle.ref_contiguous(x["a"], x["sfa"], x["b"], x["sfb"], mi, rows=rows, cols=cols)
     assert w.all()
     rep = oracle.assert_close(take(d, rows, cols), ref, "contiguous full size")
@@ -90,9 +125,11 @@ def test_masked_decode_full_size(j, n, k, poison):
     assert (bits[~written] == sentinel_of(d)).all()
     assert torch.isfinite(d[torch.from_numpy(written).to(d.device)].float()).all()
     rng = np.random.default_rng(300 + j)
-    groups = rng.choice(16, 4, replace=False)
-    cols = _sample(rng, n, 512, must=(0, n - 1))
+    groups = np.arange(16)  # every group, every valid row
+    cols = _cover(rng, n, COL_PERIODS, must=(0, n - 1))
+    _assert_covers(cols, n, COL_PERIODS, what="cols")
     ref, w = oracle.ref_masked(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
+    assert w.sum(axis=1).tolist() == [int(v) for v in mm], "every valid row of every group is compared"
     got = np.stack([take(d[int(g)], np.arange(256), cols) for g in groups])
     rep = oracle.assert_close(got[w], ref[w], f"masked full size j={j}")
     note(f"  worst={rep['worst_ratio']:.3f} cos_dist={rep['cos_dist']:.2e} masked_m={x['masked_m'].tolist()}")
@@ -106,8 +143,10 @@ def test_dense_sweep_ue8m0_full_size(i):
     d = run_dense(x)
     assert torch.isfinite(d.float()).all()
     rng = np.random.default_rng(2000 + i)
-    rows = _sample(rng, m, 48, must=(0, m - 1))
-    cols = _sample(rng, n, 768, must=range(n - 70, n))
+    rows = _cover(rng, m, ROW_PERIODS, must=(0, m - 1))
+    cols = _cover(rng, n, COL_PERIODS, must=range(n - 70, n))
+    _assert_covers(rows, m, ROW_PERIODS, what="rows")
+    _assert_covers(cols, n, COL_PERIODS, what="cols")
     ref = oracle.ref_dense_ue8m0(x["a"], x["sfa"], x["b"], x["sfb"], rows=rows, cols=cols)
     rep = oracle.assert_close(take(d, rows, cols), ref, f"dense ue8m0 M={m} N={n} K={k}")
     note(f"  worst={rep['worst_ratio']:.3f} cos_dist={rep['cos_dist']:.2e} sampled={rep['n']}")
@@ -121,9 +160,10 @@ def test_contiguous_moe_ue8m0_full_size():
     written = mi >= 0
     assert (raw_bits(d)[~written] == sentinel_of(d)).all()
     rng = np.random.default_rng(23)
-    rows = _sample(rng, x["m_total"], 64, must=())
-    rows = rows[written[rows]]
-    cols = _sample(rng, 4096, 512, must=(0, 4095))
+    rows = _cover(rng, x["m_total"], ROW_PERIODS, valid=written)
+    cols = _cover(rng, 4096, COL_PERIODS, must=(0, 4095))
+    _assert_covers(rows, x["m_total"], ROW_PERIODS, valid=written, what="rows")
+    _assert_covers(cols, 4096, COL_PERIODS, what="cols")
     ref, w = oracle.ref_contiguous_ue8m0(x["a"], x["sfa"], x["b"], x["sfb"], mi, rows=rows, cols=cols)
     assert w.all()
     rep = oracle.assert_close(take(d, rows, cols), ref, "contiguous ue8m0 full size")
@@ -138,8 +178,9 @@ def test_masked_decode_ue8m0_full_size():
     written = np.arange(256)[None, :] < mm[:, None]
     assert (raw_bits(d)[~written] == sentinel_of(d)).all()
     rng = np.random.default_rng(301)
-    groups = rng.choice(16, 3, replace=False)
-    cols = _sample(rng, 4096, 512, must=(0, 4095))
+    groups = np.arange(16)
+    cols = _cover(rng, 4096, COL_PERIODS, must=(0, 4095))
+    _assert_covers(cols, 4096, COL_PERIODS, what="cols")
     ref, w = oracle.ref_masked_ue8m0(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"], groups=groups, cols=cols)
     got = np.stack([take(d[int(g)], np.arange(256), cols) for g in groups])
     rep = oracle.assert_close(got[w], ref[w], "masked ue8m0 full size")
@@ -153,8 +194,10 @@ def test_k_grouped_wgrad_full_size():
     d = run_k_grouped(x, with_c=True)
     assert torch.isfinite(d).all()
     rng = np.random.default_rng(55)
-    rows = _sample(rng, 4096, 24, must=(0, 4095))
-    cols = _sample(rng, 7168, 384, must=(0, 7167))
+    rows = _cover(rng, 4096, ROW_PERIODS, must=(0, 4095))
+    cols = _cover(rng, 7168, COL_PERIODS, must=(0, 7167))
+    _assert_covers(rows, 4096, ROW_PERIODS, what="rows")
+    _assert_covers(cols, 7168, COL_PERIODS, what="cols")
     ref = oracle.ref_k_grouped(x["a"], x["sfa"], x["b"], x["sfb"], x["ks"], c=x["c"], rows=rows, cols=cols)
     for g in range(8):
         rep = oracle.assert_close(take(d[g], rows, cols), ref[g], f"k-grouped group {g}")
