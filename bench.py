@@ -537,6 +537,19 @@ def main():
                            roofline_frac_cold=c.roof_s / cold, roofline_frac_warm=c.roof_s / warm))
         print(f"bench:   {c.label}: cold {cold * 1e6:.1f} us ({c.flops / cold / 1e12:.1f} TFLOPS, "
               f"{100 * c.roof_s / cold:.1f}% of roofline), warm {warm * 1e6:.1f} us", file=sys.stderr, flush=True)
+    # the floor under every cold time: a minimal library call (M=1, N=16, K=128,
+    # 32 KFLOP) timed the same way, cold and warm
+    floor = None
+    if cases[0].x["kind"] in ("dense", "contiguous", "masked", "k_grouped"):
+        from workloads import gen_dense
+        tiny = Case(dict(label="floor", gen=lambda: gen_dense(1, 16, 128, seed=9)), dev)
+        tiny.call()
+        torch.cuda.synchronize()
+        floor = dict(us_cold=time_launches(tiny, args.timing_iters, flush) * 1e6,
+                     us_warm=time_launches(tiny, args.timing_iters) * 1e6,
+                     what="dense M=1 N=16 K=128 through the same entry point, timed like the cases")
+        print(f"bench:   launch floor: cold {floor['us_cold']:.1f} us, warm {floor['us_warm']:.1f} us",
+              file=sys.stderr, flush=True)
     del flush_buf
     dom = max(range(len(cases)), key=lambda i: cases[i].warm_s)
 
@@ -611,6 +624,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
+        "launch_floor": floor,
     }
     if step_flops > 0:
         out["config"]["pct_of_fp8_peak"] = 100.0 * value / PEAK_FP8_TFLOPS
