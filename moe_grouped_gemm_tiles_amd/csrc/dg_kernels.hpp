@@ -518,6 +518,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   constexpr bool XPRE = STAGES == 2;
   // BF16 output: paired 16-byte stores (see the epilogue)
   constexpr bool PAIRED_STORES = BF16_OUT;
+  // C enters the accumulators at the unit's start (split units: added by the reducing unit)
+  constexpr bool C_FIRST = HAS_C && !SPLIT;
+  constexpr bool C_LAST = HAS_C && !C_FIRST;
 
   const int vb = xcd_remap(blockIdx.x, gridDim.x);
   Unit u = find_unit(vb, 0), nx;
@@ -541,6 +544,42 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // C goes into the accumulators before the K loop (one batch of loads, covered
+      // by the unit's first wait), not into the epilogue, where each C load would
+      // wait alone behind the stores and prefetches in flight.  Split units leave C
+      // to the unit that finishes the tile.
+      if constexpr (C_FIRST) {
+        if (wave_live) {
+          int row0 = wrow0 + r16;
+          asm volatile("" : "+v"(row0));
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int gm = row0 + i * 16;
+            if (gm >= row_end) continue;
+            const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+              if (gn >= p.n) continue;
+              if constexpr (BF16_OUT) {
+                add_c_bf16(p, crow, gn, acc[i][j]);
+              } else {
+                const float* C = reinterpret_cast<const float*>(p.c) + crow + gn;
+                if (gn + 4 <= p.n) {
+                  acc[i][j] = *reinterpret_cast<const f32x4*>(C);
+                } else {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r)
+                    if (gn + r < p.n) acc[i][j][r] = C[r];
+                }
+              }
+            }
+          }
+        }
+        // every path into the K loop or straight to the epilogue (no slabs) sees C landed;
+        // the unit's first wait covers the same loads anyway
+        wait_vmcnt<0>();
+      }
 
       // K loop.  One workgroup barrier per slab, placed inside the slab's
       // MFMAs: part 1 multiplies fragment rows 0 .. FIRST-1 (row-major,
@@ -840,7 +879,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             // row_ok; the swaps run before the row test, on the whole wave.
 #pragma unroll
             for (int j = 0; j + 1 < FN; j += 2) {
-              if (HAS_C && row_ok) {  // C in the MFMA layout: this lane's row, columns 4 * q4 ..
+              if (C_LAST && row_ok) {  // C in the MFMA layout: this lane's row, columns 4 * q4 ..
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                   const int gc = n0 + wn * TN + (j + h) * 16 + 4 * q4;
@@ -867,7 +906,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             }
             if constexpr (FN % 2 == 1) {
               const int gn = n0 + wn * TN + (FN - 1) * 16 + 4 * q4;
-              if (row_ok && gn < p.n) store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][FN - 1]);
+              if (row_ok && gn < p.n) store_out<BF16_OUT, C_LAST>(p, crow, gn, drow, acc[i][FN - 1]);
             }
           } else {
             if (!row_ok) continue;
@@ -875,7 +914,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
             for (int j = 0; j < FN; ++j) {
               const int gn = n0 + wn * TN + j * 16 + 4 * q4;
               if (gn >= p.n) continue;
-              store_out<BF16_OUT, HAS_C>(p, crow, gn, drow, acc[i][j]);
+              store_out<BF16_OUT, C_LAST>(p, crow, gn, drow, acc[i][j]);
             }
           }
         }
