@@ -440,7 +440,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
     r.SFA = p.sfa + (MODE == MODE_MASKED ? (int64_t)u.g * p.sfa_gs : 0) + u.m0;
     r.B = p.b + (B_GROUPED ? (int64_t)u.g * p.b_gs : 0) + (int64_t)u.n0 * p.ldb;
     r.SFB = p.sfb + (B_GROUPED ? (int64_t)u.g * p.sfb_gs : 0);
-    r.a_rows = p.m - u.m0;
+    // masked groups: A rows at or past masked_m are read as zeros without touching
+    // memory (their outputs are never written and no other row depends on them)
+    r.a_rows = (MODE == MODE_MASKED ? u.row_end : p.m) - u.m0;
     r.b_rows = p.n - u.n0;
     // B-scale words staged with each slab: slot v holds block min(n0/128 + v, NBLK-1)
     // (clamped: columns past N are never stored)
