@@ -122,6 +122,7 @@ _SIGNATURES = {
     "dg_set_num_cus": (_i32, [_i32]),
     "dg_get_num_cus": (_i32, []),
     "dg_internal_set_tile_n": (_i32, [_i32]),
+    "dg_internal_dense_plan": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "dg_status_string": (ctypes.c_char_p, [_i32]),
     "dg_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -542,6 +543,16 @@ def _set_tile_n_for_tests(w: int):
     """Force the width of the 256-row tiles (256, 224 or 160; 0 = chosen per call).
     Not part of the API: the tests use it to cover every tile width."""
     _check(load_library().dg_internal_set_tile_n(w))
+
+
+def _dense_plan_for_tests(m: int, n: int, k: int, cus: int) -> dict:
+    """The tile, K split and workspace size a dense call of this shape gets on a
+    device with `cus` usable CUs.  Not part of the API: the tests pin the planner."""
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    ws = ctypes.c_size_t(0)
+    _check(load_library().dg_internal_dense_plan(m, n, k, cus, *[ctypes.byref(v) for v in vals], ctypes.byref(ws)))
+    bm, bn, splits, sps = (v.value for v in vals)
+    return dict(bm=bm, bn=bn, splits=splits, slabs_per_split=sps, ws_bytes=ws.value)
 
 
 # The README's names for the same utilities ("Utilities": set_num_sms / get_num_sms cap the

@@ -85,7 +85,7 @@ using KernelFn = void (*)(dg::Params);
 // The split-K configurations stream B from HBM; two independent workgroups
 // per CU keep four slabs in flight per CU.
 enum TileId { TILE_256x256 = 0, TILE_128x128 = 1, TILE_SK_128x64 = 2, TILE_SK_64x128 = 3, TILE_256x224 = 4,
-              TILE_256x160 = 5 };
+              TILE_256x160 = 5, TILE_SK_128x128 = 6 };
 
 struct Cfg {
   TileId id;
@@ -98,6 +98,7 @@ constexpr Cfg kCfg256x160{TILE_256x160, 256, 160, 4, 2, 2, 1};
 constexpr Cfg kCfg128{TILE_128x128, 128, 128, 2, 2, 2, 2};
 constexpr Cfg kCfgSk128{TILE_SK_128x64, 128, 64, 2, 2, 3, 2};
 constexpr Cfg kCfgSk64{TILE_SK_64x128, 64, 128, 1, 4, 3, 2};
+constexpr Cfg kCfgSk128x128{TILE_SK_128x128, 128, 128, 2, 2, 3, 1};
 
 // Output flavour of a launch.
 struct Epi {
@@ -108,9 +109,9 @@ struct Epi {
 // dense: every tile, BF16/FP32, with/without C (the skinny tiles split K);
 // M-grouped: the 256-row tiles and 128x128 without C; K-grouped: FP32
 // with/without C.
-template <int BM, int BN, int WM, int WN, int ST, int MODE, bool E8M0>
+template <int BM, int BN, int WM, int WN, int ST, int MODE, bool E8M0, bool SPLIT_TILE = false>
 KernelFn pick_out(const Epi& e) {
-  constexpr bool kSplit = MODE == dg::MODE_DENSE && (BM < 128 || BN < 128);
+  constexpr bool kSplit = MODE == dg::MODE_DENSE && (SPLIT_TILE || BM < 128 || BN < 128);
   if constexpr (MODE == dg::MODE_DENSE) {
     if (e.bf16)
       return e.has_c ? dg::gemm_kernel<BM, BN, WM, WN, ST, MODE, kSplit, true, true, E8M0>
@@ -131,6 +132,7 @@ KernelFn pick_tile(const Cfg& c, const Epi& e) {
   if constexpr (MODE == dg::MODE_DENSE) {
     if (c.id == TILE_SK_128x64) return pick_out<128, 64, 2, 2, 3, MODE, E8M0>(e);
     if (c.id == TILE_SK_64x128) return pick_out<64, 128, 1, 4, 3, MODE, E8M0>(e);
+    if (c.id == TILE_SK_128x128) return pick_out<128, 128, 2, 2, 3, MODE, E8M0, true>(e);
   }
   if (c.id == TILE_256x256) return pick_out<256, 256, 2, 4, 2, MODE, E8M0>(e);
   if (c.id == TILE_256x224) return pick_out<256, 224, 4, 2, 2, MODE, E8M0>(e);
@@ -176,35 +178,32 @@ Cfg choose_wide(int64_t row_tiles, int n, int slots) {
   return best;
 }
 
-// Split count for a skinny dense GEMM.  Estimated time, in slab times: rounds
-// of units at one unit per CU x (slabs per split + ~6 slabs of pipeline fill
-// and latency per unit), plus ~0.5 slab time per extra split for the partials
-// the last unit of each tile reads back.  Fitted to cold timings of the
-// dense-sweep shapes with M <= 128 over forced split counts 1..32: the best
-// counts keep about one unit per CU (a second unit on a CU shares its memory
-// pipeline) and stop short of many small splits.  Splits that would make more
-// than two units per CU are not considered (splitting pays only while the
-// tiles leave CUs idle), which also bounds the workspace to 2 x CUs partial
-// tiles.
-int choose_splits(int tiles, int kb, int cus, int* slabs_per_split) {
-  int best_s = 1, best_sps = kb;
-  double best_cost = 1e300;
-  for (int s = 1; s <= kb; ++s) {
-    const int sps = cdiv(kb, s);
-    const int s_eff = cdiv(kb, sps);
-    if (s_eff != s) continue;
-    if (s > 1 && static_cast<int64_t>(tiles) * s > 2ll * cus) break;
-    const int rounds = cdiv(tiles * s_eff, cus);
-    const double cost = static_cast<double>(rounds) * (sps + 6.0) + 0.5 * (s_eff - 1);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best_s = s_eff;
-      best_sps = sps;
-    }
+// Skinny dense GEMMs (M <= 128) split K over workgroups.  Estimated time of a
+// (tile, splits) candidate, in microseconds, from per-unit timelines taken with
+// s_memrealtime stamps on MI355X: ~2.5 us from launch to a unit's first slab,
+// then one slab per (BM + BN) x 128 B / 36 GB/s (what one CU sustains for these
+// row-strided direct loads, whatever the ring depth), ~1.7 us to publish a
+// partial, and the last unit of a tile reading every partial at ~85 GB/s.
+// Units beyond one per CU wait for a round (two on one CU share its loads).
+// A 128-column tile reads each A slab half as often per B byte as a 64-column
+// one but makes fewer tiles (more splits) and larger partials.
+double skinny_cost(const Cfg& c, int64_t tiles, int kb, int s, int cus) {
+  const int sps = cdiv(kb, s);
+  const int64_t rounds = (tiles * s + cus - 1) / cus;
+  const double slab_us = (c.bm + c.bn) * 128.0 / 36e3;
+  double unit_us = 2.5 + (sps - 1) * slab_us;
+  double tail_us = 0.0;
+  if (s > 1) {
+    unit_us += 1.7;
+    tail_us = s * static_cast<double>(c.bm) * c.bn * sizeof(float) / 85e3;
   }
-  *slabs_per_split = best_sps;
-  return best_s;
+  return static_cast<double>(rounds) * unit_us + tail_us;
 }
+
+// Partials of one call: at most 16 MiB (two 128x64 / 64x128 units or one
+// 128x128 unit per CU of a 256-CU device), which is also the allocation-free
+// entry point's scratch, so both entry points make the same plans.
+constexpr size_t kMaxPartialBytes = size_t(16) << 20;
 
 // Tile configuration and K split of a dense call, and the workspace the split needs.
 struct DensePlan {
@@ -213,27 +212,50 @@ struct DensePlan {
   size_t ws_bytes;  // 0: no split, no workspace
 };
 
+// The plan on a device with `cus` usable CUs (host arithmetic only).
+DensePlan plan_dense_for(int m, int n, int k, int cus) {
+  DensePlan pl{};
+  pl.splits = 1;
+  pl.slabs_per_split = k / 128;
+  pl.ws_bytes = 0;
+  if (m > 128) {
+    pl.cfg = n > 128 ? choose_wide(cdiv(m, 256), n, cus) : kCfg128;
+    return pl;
+  }
+  // Skinny: every candidate tile and split count (splits that would put more than
+  // two units on a CU are not considered: splitting pays only while tiles leave CUs idle).
+  const Cfg cands[2] = {m <= 64 ? kCfgSk64 : kCfgSk128, kCfgSk128x128};
+  const int ncand = m <= 64 ? 1 : 2;
+  const int kb = k / 128;
+  double best = 1e300;
+  pl.cfg = cands[0];
+  for (int ci = 0; ci < ncand; ++ci) {
+    const Cfg& c = cands[ci];
+    const int64_t tiles = static_cast<int64_t>(cdiv(m, c.bm)) * cdiv(n, c.bn);
+    if (tiles <= 0) continue;
+    for (int s = 1; s <= kb; ++s) {
+      const int sps = cdiv(kb, s);
+      if (cdiv(kb, sps) != s) continue;  // each split count once, as its slabs per split
+      const size_t part = static_cast<size_t>(s) * tiles * c.bm * c.bn * sizeof(float);
+      if (s > 1 && (tiles * s > 2ll * cus || part > kMaxPartialBytes || tiles > kCtrWords)) break;
+      const double cost = skinny_cost(c, tiles, kb, s, cus);
+      if (cost < best - 1e-9) {
+        best = cost;
+        pl.cfg = c;
+        pl.splits = s;
+        pl.slabs_per_split = sps;
+        pl.ws_bytes = s > 1 ? kCtrBytes + part : 0;
+      }
+    }
+  }
+  return pl;
+}
+
 dg_status plan_dense(int m, int n, int k, DensePlan* out) {
   int cus = 0;
   dg_status st = usable_cus(&cus);
   if (st != DG_SUCCESS) return st;
-  DensePlan pl{};
-  pl.cfg = m <= 64 ? kCfgSk64 : m <= 128 ? kCfgSk128 : (n > 128 ? choose_wide(cdiv(m, 256), n, cus) : kCfg128);
-  pl.splits = 1;
-  pl.slabs_per_split = k / 128;
-  pl.ws_bytes = 0;
-  const bool skinny = pl.cfg.id == TILE_SK_128x64 || pl.cfg.id == TILE_SK_64x128;
-  const int64_t tiles = static_cast<int64_t>(cdiv(m, pl.cfg.bm)) * cdiv(n, pl.cfg.bn);
-  if (skinny && k >= 128 * 2 && tiles > 0 && tiles <= kCtrWords) {
-    int sps = 0;
-    const int s = choose_splits(static_cast<int>(tiles), k / 128, cus, &sps);
-    if (s > 1) {
-      pl.splits = s;
-      pl.slabs_per_split = sps;
-      pl.ws_bytes = kCtrBytes + static_cast<size_t>(s) * tiles * pl.cfg.bm * pl.cfg.bn * sizeof(float);
-    }
-  }
-  *out = pl;
+  *out = plan_dense_for(m, n, k, cus);
   return DG_SUCCESS;
 }
 
@@ -483,11 +505,10 @@ dg_status k_grouped_impl(const void* a, const void* sfa, int64_t ld_sfa, const v
 
 // ---- allocation-free dense entry point ---------------------------------------
 // Split-K scratch of dg_fp8_gemm_nt_noalloc: counters then partials, the
-// largest workspace plan_dense asks for on a 256-CU device (two units per CU
-// of 32 KiB partial tiles).  Each device holds its own copy; its address comes
+// largest workspace plan_dense asks for (kMaxPartialBytes of partials).  Each device holds its own copy; its address comes
 // from hipGetSymbolAddress on that device (the name itself is only a host-side
 // stand-in) and is kept per device.
-constexpr size_t kScratchBytes = kCtrBytes + (size_t(16) << 20);
+constexpr size_t kScratchBytes = kCtrBytes + kMaxPartialBytes;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 std::mutex g_scratch_mutex;
@@ -662,6 +683,20 @@ int dg_get_num_cus(void) {
     return cap;  // no device: the cap (0 = uncapped)
   }
   return (cap > 0 && cap < total) ? cap : total;
+}
+
+dg_status dg_internal_dense_plan(int m, int n, int k, int cus, int* bm, int* bn, int* splits, int* slabs_per_split,
+                                 size_t* ws_bytes) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || cus <= 0) return DG_ERROR_INVALID_VALUE;
+  if (bm == nullptr || bn == nullptr || splits == nullptr || slabs_per_split == nullptr || ws_bytes == nullptr)
+    return DG_ERROR_INVALID_VALUE;
+  const DensePlan pl = plan_dense_for(m, n, k, cus);
+  *bm = pl.cfg.bm;
+  *bn = pl.cfg.bn;
+  *splits = pl.splits;
+  *slabs_per_split = pl.slabs_per_split;
+  *ws_bytes = pl.ws_bytes;
+  return DG_SUCCESS;
 }
 
 dg_status dg_internal_set_tile_n(int tile_n) {

@@ -15,6 +15,12 @@ extern "C" {
 // DG_ERROR_INVALID_VALUE.
 dg_status dg_internal_set_tile_n(int tile_n);
 
+// The tile (bm x bn), K split (splits x slabs_per_split slabs of 128) and
+// workspace bytes a dense call of this shape gets on a device with `cus` usable
+// CUs.  Host arithmetic only.  Bad sizes or null outputs -> DG_ERROR_INVALID_VALUE.
+dg_status dg_internal_dense_plan(int m, int n, int k, int cus, int* bm, int* bn, int* splits, int* slabs_per_split,
+                                 size_t* ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -817,43 +817,45 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
           __syncthreads();
           epilogue = s_last != 0;
           if (epilogue && wave_live) {
-            // acc = partial 0 + partial 1 + ... in split order (this unit's own
-            // partial from registers); the next partial's loads are issued
-            // before the current one is added.
-            f32x4 sum[FM][FN], nxt[FM][FN];
-            auto fetch = [&](int s) {
-              if (s == u.split) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                  for (int j = 0; j < FN; ++j) nxt[i][j] = acc[i][j];
-              } else {
-                const auto rs = unit_rsrc(s);
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                  for (int j = 0; j < FN; ++j)
-                    nxt[i][j] = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, loff + (i * FN + j) * 1024, 0, SC1));
-              }
-            };
-            fetch(0);
-            for (int s = 0; s < p.splits; ++s) {
-              f32x4 cur[FM][FN];
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) cur[i][j] = nxt[i][j];
-              if (s + 1 < p.splits) fetch(s + 1);
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) sum[i][j] = s == 0 ? cur[i][j] : sum[i][j] + cur[i][j];
-            }
+            // acc = partial 0 + partial 1 + ... in split order: this unit's own
+            // partial from registers, the others read back from the workspace, two
+            // in flight (one CU's read rate, not the latency, bounds this loop).
+            // The own partial's fetch gets an empty descriptor (no memory access), so
+            // every step issues the same loads and the compiler's waits stay counted.
+            constexpr int RD = 2;
+            f32x4 own[FM][FN], buf[RD][FM][FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-              for (int j = 0; j < FN; ++j) acc[i][j] = sum[i][j];
+              for (int j = 0; j < FN; ++j) own[i][j] = acc[i][j];
+            auto fetch = [&](int s, f32x4 (&dst)[FM][FN]) {
+              const auto rs = (s < p.splits && s != u.split) ? unit_rsrc(s) : make_rsrc(p.ws, 0u);
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  dst[i][j] = __builtin_bit_cast(
+                      f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, loff + (i * FN + j) * 1024, 0, SC1));
+            };
+#pragma unroll
+            for (int r = 0; r < RD; ++r) fetch(r, buf[r]);
+            for (int s0 = 0; s0 < p.splits; s0 += RD) {
+#pragma unroll
+              for (int r = 0; r < RD; ++r) {
+                const int s = s0 + r;
+                if (s < p.splits) {
+                  const bool mine = s == u.split;
+#pragma unroll
+                  for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                      const f32x4 v = mine ? own[i][j] : buf[r][i][j];
+                      acc[i][j] = s == 0 ? v : acc[i][j] + v;
+                    }
+                }
+                fetch(s + RD, buf[r]);
+              }
+            }
           }
           wait_vmcnt<0>();
         }

@@ -66,9 +66,35 @@ def test_wgrad_split_k_in_place():
 
 def test_small_shapes_split():
     for m, n, k in ((1, 2112, 7168), (64, 2112, 7168), (64, 7168, 2048), (100, 1040, 4096), (128, 4096, 7168),
-                    (33, 300, 512)):
+                    (128, 7168, 16384)):
         assert dg.get_workspace_size(m, n, k) > 0, f"M={m} N={n} K={k} expected to split K"
     assert dg.get_workspace_size(129, 4096, 7168) == 0  # M > 128: no split
+
+
+@pytest.mark.parametrize("m,n,k,cap,out,with_c,in_place", [
+    (128, 1005, 8192, 32, "bf16", True, False), (100, 520, 8192, 24, "fp32", True, True),
+    (96, 1005, 4096, 32, "bf16", False, False), (128, 520, 4096, 16, "fp32", False, False),
+    (128, 1005, 8192, 48, "fp32", True, False)])
+def test_128_column_split_tile(m, n, k, cap, out, with_c, in_place):
+    """64 < M <= 128 on a CU cap where the planner takes 128x128 tiles with K split:
+    D (with or without C, in place or not) against the oracle, columns past N untouched."""
+    plan = dg._dense_plan_for_tests(m, n, k, cap)
+    assert (plan["bm"], plan["bn"]) == (128, 128) and plan["splits"] > 1, plan
+    note(f"128x128 split M={m} N={n} K={k} cap={cap} {out} C={with_c} in_place={in_place}: {plan}")
+    x = gen_dense(m, n, k, seed=7 * m + n + k, with_c=with_c, out_dtype=out)
+    ref = oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"))
+    try:
+        dg.set_num_cus(cap)
+        assert dg.get_workspace_size(m, n, k) == plan["ws_bytes"]
+        d = run_dense(x, ld_d=1024, c_in_place=in_place)
+        d2 = run_dense(x, ld_d=1024, c_in_place=in_place)
+    finally:
+        dg.set_num_cus(0)
+    oracle.assert_close(as_f64(d), ref, f"128x128 split M={m} N={n} K={k}")
+    assert np.array_equal(raw_bits(d), raw_bits(d2)), "not deterministic"
+    full = d.as_strided((m, 1024), (1024, 1))
+    pad = 0 if in_place else sentinel_of(d)  # C's padding is zero-filled
+    assert (raw_bits(full)[:, n:] == pad).all(), "columns past N were written"
 
 
 def test_one_workspace_serves_a_sequence_of_shapes():
