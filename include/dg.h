@@ -39,8 +39,9 @@
  *     never an error: out-of-range values are clamped or skipped so that all
  *     memory accesses stay in bounds.
  *
- * Workspace: skinny dense GEMMs (M <= 128, K >= 512) split K across
- * workgroups.  Each workgroup writes the FP32 partial sum of its K range to a
+ * Workspace: skinny dense GEMMs (M <= 128) may split K across workgroups (the
+ * library decides per shape and CU count; a call splits exactly when
+ * dg_get_workspace_size is not 0).  Each workgroup writes the FP32 partial sum of its K range to a
  * caller-owned workspace and counts itself in a per-tile counter there; the
  * workgroup that completes a tile adds the partials in K-range order (so the
  * result is deterministic), writes D and resets the counter.  One launch per
@@ -115,9 +116,9 @@ dg_status dg_fp8_gemm_nt(const void* a, int64_t lda, const float* sfa, int64_t l
  *     wrong results; order them (one stream).
  *   - Each split call first clears the counters it uses (one small kernel on
  *     `stream`), so a call does not depend on what the previous one left.
- *   - A call that needs more scratch than the fixed size (more than two
- *     units of 32 KiB per CU, never the case on a 256-CU device) ->
- *     DG_ERROR_SCRATCH_LIMIT, nothing enqueued.
+ *   - A call that needs more scratch than the fixed size ->
+ *     DG_ERROR_SCRATCH_LIMIT, nothing enqueued.  Every dense plan keeps its
+ *     partials within 16 MiB, so with these kernels this does not happen.
  * Arguments, layouts and other errors as for dg_fp8_gemm_nt.
  */
 dg_status dg_fp8_gemm_nt_noalloc(const void* a, int64_t lda, const float* sfa, int64_t ld_sfa,
@@ -128,8 +129,8 @@ dg_status dg_fp8_gemm_nt_noalloc(const void* a, int64_t lda, const float* sfa, i
 /*
  * Bytes of split-K workspace the dense GEMMs (dg_fp8_gemm_nt, its UE8M0 form
  * and dg_wgrad_fp8_gemm_nt) need for an M x N x K call on the current device
- * with the current CU cap; 0 when the call does not split K (M > 128, K < 512)
- * or the sizes are invalid.  One workspace serves calls of several shapes
+ * with the current CU cap (at most 64 KiB + 16 MiB); 0 when the call does not
+ * split K (always for M > 128) or the sizes are invalid.  One workspace serves calls of several shapes
  * if it is at least as large as each call's size.  Host-only, enqueues nothing.
  *   (The pages leave the workspace of split reductions unspecified; the
  *   README's calls take caller-allocated outputs, "Mega MoE" usage.)
