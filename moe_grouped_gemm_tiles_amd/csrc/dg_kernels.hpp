@@ -358,6 +358,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
   };
   // The unit (tile, pass), or the first valid one at or after it in this
   // workgroup's tile sequence.
+  // Group data (contiguous row groups, masked row counts, K sizes) is read-only
+  // for the kernel, and the unit decode reads it at uniform indices: through the
+  // constant address space those reads are scalar loads, which do not share the
+  // vector-memory counter with the slabs in flight (as vector loads each of them
+  // made the next unit's decode wait for every load issued before it).
+  const __attribute__((address_space(4))) int32_t* grp_s = (const __attribute__((address_space(4))) int32_t*)p.grp;
   auto find_unit = [&](int tile, int pass) {
     Unit u;
     u.tile = -1;
@@ -377,9 +383,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         // group g's K blocks start after the blocks of groups 0..g-1; sizes are
         // device data, so they are clamped into [0, KB] rather than trusted
         int off = 0;
-        for (int h = 0; h < g; ++h) off += max(p.grp[h], 0) >> 7;
+        for (int h = 0; h < g; ++h) off += max(grp_s[h], 0) >> 7;
         kb_begin = min(off, KB);
-        kb_end = min(kb_begin + (max(p.grp[g], 0) >> 7), KB);
+        kb_end = min(kb_begin + (max(grp_s[g], 0) >> 7), KB);
       }
       int mb, nb;
       raster<4>(t, p.tiles_m, p.tiles_n, mb, nb);
@@ -387,12 +393,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       // groups served by this tile (contiguous: one per 128-row half)
       int row_end = p.m, g0 = 0, g1 = 0, passes = 1;
       if (MODE == MODE_MASKED) {
-        const int mm = min(max(p.grp[g], 0), p.m);
+        const int mm = min(max(grp_s[g], 0), p.m);
         if (m0 >= mm) continue;
         row_end = mm;
       } else if (MODE == MODE_CONTIG) {
-        g0 = p.grp[m0];
-        g1 = (BM == 256 && m0 + 128 < p.m) ? p.grp[m0 + 128] : -1;
+        g0 = grp_s[m0];
+        g1 = (BM == 256 && m0 + 128 < p.m) ? grp_s[m0 + 128] : -1;
         if (g0 < 0 || g0 >= p.num_groups) g0 = -1;
         if (g1 < 0 || g1 >= p.num_groups) g1 = -1;
         if (g0 < 0 && g1 < 0) continue;
@@ -551,7 +557,31 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       // wait alone behind the stores and prefetches in flight.  Split units leave C
       // to the unit that finishes the tile.
       if constexpr (C_FIRST) {
-        if (wave_live) {
+        // A tile wholly inside D (every row and column of it valid) loads C in one
+        // batch with no branches; with a branch around each load (the edge tests
+        // below) the compiler waited for the loads a few at a time.  Same values
+        // either way: FP32 C is assigned, BF16 C added to the zeroed accumulators.
+        const bool inside = m0 + BM <= row_end && n0 + BN <= p.n;
+        if (wave_live && inside) {
+          const int row0 = wrow0 + r16;
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)(row0 + i * 16) * p.ldc;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int gn = n0 + wn * TN + j * 16 + 4 * q4;
+              if constexpr (BF16_OUT) {
+                const uint2 cv = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.c) + crow + gn);
+                acc[i][j][0] += __uint_as_float(cv.x << 16);
+                acc[i][j][1] += __uint_as_float(cv.x & 0xFFFF0000u);
+                acc[i][j][2] += __uint_as_float(cv.y << 16);
+                acc[i][j][3] += __uint_as_float(cv.y & 0xFFFF0000u);
+              } else {
+                acc[i][j] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.c) + crow + gn);
+              }
+            }
+          }
+        } else if (wave_live) {
           int row0 = wrow0 + r16;
           asm volatile("" : "+v"(row0));
 #pragma unroll
@@ -768,13 +798,33 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       stage_barrier();  // all LDS reads of this unit are done before the next unit's loads
       debug_fence();
 
+      // Contiguous: the group of each row this lane stores, loaded before the next
+      // unit's slabs are prefetched (the vector-memory counter completes in issue
+      // order, so loaded in the epilogue they waited for the prefetched slabs too).
+      // Every lane loads, at a clamped row, so that no load sits in a branch (which
+      // made the compiler wait for each); the epilogue's row test rejects rows past
+      // row_end.
+      int row_grp[MODE == MODE_CONTIG ? FM : 1];
+      if constexpr (MODE == MODE_CONTIG) {
+        const int row0 = wrow0 + r16;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) row_grp[i] = p.grp[min(row0 + i * 16, row_end - 1)];
+        asm volatile("" ::: "memory");  // the loads above precede the prefetch below
+      }
+
       // next unit: its first two slabs go out before this unit's stores
       nx = next_unit(u);
-      if (XPRE && nx.tile >= 0 && nx.kb_end > nx.kb_begin) {
-        const Src ns = src_of(nx);
-        issue_slab(ns, nx.kb_begin, 0, true);
-        issue_slab(ns, nx.kb_begin + 1, 1, nx.kb_begin + 1 < nx.kb_end);
-        pre_next = 1;
+      if constexpr (XPRE) {
+        // Issued on every path, with empty descriptors when there is no next unit,
+        // so that the loads in flight are the same wherever the compiler counts the
+        // epilogue's waits (with the prefetch in a branch it fell back to waiting for
+        // most of it).  The stages are free: every wave is past the last barrier.
+        const bool has_next = nx.tile >= 0 && nx.kb_end > nx.kb_begin;
+        const Src ns = src_of(has_next ? nx : u);
+        const int kb0 = has_next ? nx.kb_begin : u.kb_begin;
+        issue_slab(ns, kb0, 0, has_next);
+        issue_slab(ns, kb0 + 1, 1, has_next && nx.kb_begin + 1 < nx.kb_end);
+        pre_next = has_next ? 1 : 0;
         asm volatile("" ::: "memory");  // the prefetch precedes every store below
       }
 
@@ -871,7 +921,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
         for (int i = 0; i < FM; ++i) {
           const int gm = row0 + i * 16;
           bool row_ok = gm < row_end;
-          if (MODE == MODE_CONTIG) row_ok = row_ok && p.grp[gm] == g;
+          if constexpr (MODE == MODE_CONTIG) row_ok = row_ok && row_grp[i] == g;
           const int64_t drow = (MODE == MODE_MASKED || MODE == MODE_KGROUP ? (int64_t)g * p.d_gs : 0) + (int64_t)gm * p.ldd;
           const int64_t crow = (MODE == MODE_KGROUP ? (int64_t)g * p.c_gs : 0) + (int64_t)gm * p.ldc;
           if constexpr (PAIRED_STORES) {
@@ -929,6 +979,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
     u = nx;
     pre = pre_next;
   }
+  wait_vmcnt<0>();  // no direct load into this workgroup's LDS outlives it
 }
 
 }  // namespace dg
