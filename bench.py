@@ -57,12 +57,38 @@ COPY_CAL_MB = 256  # plain device-to-device copy used to calibrate FETCH_SIZE / 
 TIMED_MARK = "timed: "  # roctx range name prefix of the timed launches of the dominant case
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without comments and with runs of whitespace collapsed (string
+    and character literals kept), so that editing a comment does not change the hash."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(family: str) -> str:
+    """Hash of the sources of a kernel family, comments and whitespace excluded."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,7 +12,7 @@
 //   overlap the matrix instructions.
 //
 // Design (gfx950; measured: FP8 MFMA ~4.0-4.6 PFLOP/s sustained depending on
-// clock, LDS b128 reads ~200 B/clk/CU, direct global->LDS loads ~60 B/clk/CU):
+// clock, LDS b128 reads ~157 B/clk/CU, direct global->LDS loads ~60 B/clk/CU):
 //   * A workgroup owns a BM x BN output tile and walks K in 128-wide slabs;
 //     each slab is exactly one scale block along K.
 //   * Staging: buffer_load_dwordx4 ... lds copies each slab of A and B (and
@@ -34,8 +34,8 @@
 //     value per lane per 16-row fragment and stores are 8/16-byte vectors.
 //   * FP32 scales: each slab's partial comes out of the MFMA with a zero
 //     accumulator and is promoted, acc += P * (sfa[row] * sfb[block]), with
-//     FP32 FMAs.  The FMAs of MFMA t are issued after MFMA t+2 (a 3-deep ring
-//     of partials), so the promotion runs under the matrix core.
+//     FP32 FMAs.  The FMAs of MFMA t are issued after MFMA t+3 (a ring of four
+//     partials), so the promotion runs under the matrix core.
 //   * UE8M0 scales (powers of two): the MFMA's own block-scale operands apply
 //     sfa (per lane = per A row) and sfb (uniform per wave) to every 32-K
 //     chunk of the slab, and the MFMA accumulates straight into acc: no
@@ -614,17 +614,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_kernel(const Params p) {
       }
 
       // K loop.  One workgroup barrier per slab, placed inside the slab's
-      // MFMAs: part 1 multiplies fragment rows 0 .. FIRST-1 (row-major,
-      // A fragments streamed from LDS) and reads the slab's last HOLD A
-      // fragments into registers; at the barrier every wave has finished
-      // reading slab `it` (its stage takes slab it + STAGES) and slab it + 1 has
-      // landed; part 2 multiplies rows FIRST .. FM-1 (column-major) from
-      // registers only, issuing one direct load of slab it + STAGES per MFMA
-      // (with two stages only the first P2L; the rest go out at the start of
-      // the next part 1) and reading slab it + 1's B fragments, first A
-      // fragment and scales as the columns free up.  No LDS latency and no
-      // burst of loads sits at the barrier.  Each slab's FP32 promotion trails its MFMAs by LAG and
-      // carries across the slab boundary.
+      // MFMAs.  The outer fragments (the operand with fewer fragments per wave)
+      // stay in registers for the slab; the inner ones are streamed.  Part 1
+      // multiplies inner fragments 0 .. FIRST-1 (inner-major), streaming them
+      // from LDS, and reads the last HOLD inner fragments into registers; at
+      // the barrier every wave has finished reading slab `it` (its stage takes
+      // slab it + STAGES) and slab it + 1 has landed; part 2 multiplies the HOLD
+      // held fragments (outer-major) from registers only, issuing one direct
+      // load of slab it + STAGES per MFMA (with two stages only the first P2L;
+      // the rest go out at the start of the next part 1) and reading slab
+      // it + 1's outer fragments and first inner fragment as they free up.  No
+      // LDS latency and no burst of loads sits at the barrier.  Each slab's FP32
+      // promotion trails its MFMAs by LAG and carries across the slab boundary.
       // inner / outer fragment of the slab's MFMA t (part 1: inner-major over
       // the streamed fragments, part 2: outer-major over the held ones), and
       // the output fragment row / column they give
