@@ -208,3 +208,49 @@ def test_masked_one_scale_row_needs_aligned_row_length():
     ref, written = oracle.ref_masked(x["a"], x["sfa"], x["b"], x["sfb"], x["masked_m"])
     oracle.assert_close(as_f64(d)[written], ref[written], "masked K=128")
     assert (raw_bits(d)[~written] == sentinel_of(d)).all()
+
+
+def _cap_for_128_column_split(m, n, k):
+    """A CU cap under which the planner gives this shape 128x128 tiles with K split."""
+    for cap in (8, 12, 16, 24, 32, 48, 64):
+        plan = dg._dense_plan_for_tests(m, n, k, cap)
+        if (plan["bm"], plan["bn"]) == (128, 128) and plan["splits"] > 1:
+            return cap, plan
+    pytest.fail(f"no CU cap gives a 128x128 split plan for M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m,n,out,with_c", [(128, 1005, "bf16", False), (100, 520, "fp32", True)])
+def test_128_column_split_tile_ue8m0(m, n, out, with_c):
+    """The UE8M0 entry point on the 128x128 split tile (block-scaled MFMAs, partials
+    reduced in split order) against the UE8M0 oracle."""
+    k = 8192
+    cap, plan = _cap_for_128_column_split(m, n, k)
+    note(f"ue8m0 128x128 split M={m} N={n} K={k} cap={cap} {out} C={with_c}: {plan}")
+    x = gen_dense(m, n, k, seed=9 * m + n, with_c=with_c, out_dtype=out, scale_fmt="ue8m0")
+    ref = oracle.ref_dense_ue8m0(x["a"], x["sfa"], x["b"], x["sfb"], x.get("c"))
+    try:
+        dg.set_num_cus(cap)
+        d = run_dense(x, ld_d=1024)
+    finally:
+        dg.set_num_cus(0)
+    oracle.assert_close(as_f64(d), ref, f"ue8m0 128x128 split M={m} N={n}")
+
+
+def test_wgrad_on_128_column_split_tile():
+    """The in-place weight-gradient entry point (D += A B^T, FP32) on the 128x128 split tile."""
+    m, n, k = 128, 520, 8192
+    cap, plan = _cap_for_128_column_split(m, n, k)
+    note(f"wgrad 128x128 split M={m} N={n} K={k} cap={cap}: {plan}")
+    x = gen_dense(m, n, k, seed=1401, with_c=True, out_dtype="fp32")
+    a, sfa, b, sfb = _dev_inputs(x)
+    d = to_dev(x["c"].astype(np.float32))
+    try:
+        dg.set_num_cus(cap)
+        ws = dg.alloc_workspace(m, n, k)
+        assert ws is not None and ws.numel() == plan["ws_bytes"]
+        dg.wgrad_fp8_gemm_nt((a, sfa), (b, sfb), d, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        dg.set_num_cus(0)
+    oracle.assert_close(as_f64(d), oracle.ref_dense(x["a"], x["sfa"], x["b"], x["sfb"], x["c"]),
+                        "wgrad 128x128 split")
