@@ -400,6 +400,21 @@ class Case:
 
 
 
+class _VendorFp8:
+    """The platform's FP8 GEMM on a dense case's operands (per-tensor unit scales,
+    BF16 out): the same MFMA work without the per-slab block-scale promotion."""
+
+    def __init__(self, x: dict, dev: str):
+        import numpy as np
+        import torch
+
+        self.a = torch.from_numpy(np.ascontiguousarray(x["a"])).to(dev).view(torch.float8_e4m3fn)
+        self.b = torch.from_numpy(np.ascontiguousarray(x["b"])).to(dev).view(torch.float8_e4m3fn)
+        self.one = torch.ones((), dtype=torch.float32, device=dev)
+        self.call = lambda: torch._scaled_mm(self.a, self.b.t(), scale_a=self.one, scale_b=self.one,
+                                             out_dtype=torch.bfloat16)
+
+
 def time_launches(case: Case, iters: int, flush=None):
     """Median per-launch time (s) with HIP events on the current stream (the
     stream the library launches on)."""
@@ -498,6 +513,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=512, help="cache flush buffer for the per-shape cold timing")
     ap.add_argument("--timing-iters", type=int, default=10, help="launches per shape for the warm/cold timing")
+    ap.add_argument("--vendor-fp8", action="store_true",
+                    help="also time the platform's per-tensor-scaled FP8 GEMM (torch._scaled_mm) on each dense "
+                         "case's operands, as context (it skips the block scaling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"run one {COPY_CAL_MB} MiB device copy first (calibrates rocprofv3 byte counters)")
     ap.add_argument("--profile-summary", nargs=3, metavar=("PROF_DIR", "OUT_MD", "CASE_LABEL"),
@@ -563,6 +581,16 @@ def main():
                            roofline_frac_cold=c.roof_s / cold, roofline_frac_warm=c.roof_s / warm))
         print(f"bench:   {c.label}: cold {cold * 1e6:.1f} us ({c.flops / cold / 1e12:.1f} TFLOPS, "
               f"{100 * c.roof_s / cold:.1f}% of roofline), warm {warm * 1e6:.1f} us", file=sys.stderr, flush=True)
+        if args.vendor_fp8 and c.x["kind"] == "dense" and c.x.get("c") is None:
+            v = _VendorFp8(c.x, dev)
+            v.call()
+            torch.cuda.synchronize()
+            v_warm, v_cold = time_launches(v, args.timing_iters), time_launches(v, args.timing_iters, flush)
+            detail[-1].update(vendor_fp8_us_cold=v_cold * 1e6, vendor_fp8_us_warm=v_warm * 1e6,
+                              vendor_fp8_tflops_cold=c.flops / v_cold / 1e12)
+            print(f"bench:     per-tensor FP8 torch._scaled_mm, same operands: cold {v_cold * 1e6:.1f} us "
+                  f"({c.flops / v_cold / 1e12:.1f} TFLOPS), warm {v_warm * 1e6:.1f} us", file=sys.stderr, flush=True)
+            del v
     # the floor under every cold time: a minimal library call (M=1, N=16, K=128,
     # 32 KFLOP) timed the same way, cold and warm
     floor = None
