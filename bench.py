@@ -3,7 +3,7 @@
 
 One step = one pass of the selected workload through the library's C ABI,
 with inputs already resident in HBM.  The default workload ("baseline") is
-the five benchmark configurations, 19 calls: (0) dense M=128 N=256 K=512;
+the five benchmark configurations, 20 calls: (0) dense M=128 N=256 K=512;
 (1) the 15-shape dense sweep, M in {64, 128, 4096} x (N, K) in {(2112,7168),
 (24576,1536), (7168,16384), (4096,7168), (7168,2048)}; (2) the contiguous MoE
 GEMM, 8 groups of U[1,8192] tokens, N=4096 K=7168; (3) masked decode, 16
