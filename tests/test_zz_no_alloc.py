@@ -2,7 +2,8 @@
 the C ABI, against the workspace entry point (dg_fp8_gemm_nt) on the same inputs:
 bit-identical outputs (same kernels and split counts) and within the oracle's
 tolerance, on consecutive calls whose second input is smaller, with and without C,
-and for a shape that does not split K.
+for a shape that does not split K, and captured into a HIP graph that is replayed
+after eager calls of another shape have used the same scratch.
 """
 
 import numpy as np
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():  # pragma: no cover - GPU only
     import moe_grouped_gemm_tiles_amd as dg
-    from tests._gpu_harness import as_f64, c_tensor, fp8_dev, note, out_buffer, raw_bits, to_dev
+    from tests._gpu_harness import SENT_BF16, SENT_F32, as_f64, c_tensor, fp8_dev, note, out_buffer, raw_bits, to_dev
 
 
 def _args(x, d, c=None):
@@ -78,3 +79,56 @@ def test_noalloc_repeated_and_unsplit_shapes():
             d = out_buffer((x["m"],), x["n"], "bf16")
             _noalloc(x, d)
             assert np.array_equal(raw_bits(d), want[i]), f"repeat {rep}, input {i}"
+
+
+def _noalloc_launch(args):
+    """One call on the current stream, no synchronisation (capturable)."""
+    lib = dg.load_library()
+    st = lib.dg_fp8_gemm_nt_noalloc(*args, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.dg_status_string(st)
+
+
+def test_noalloc_captured_in_a_graph_and_replayed():
+    """The callers this entry point serves capture it: one graph holds two split-K calls
+    of different shapes (the second smaller, with C); before every replay an eager call
+    of a third shape leaves its own partials and counters in the shared scratch, and
+    every replay must still equal the workspace entry point bit for bit."""
+    calls = []
+    for (m, n, k), with_c, seed in (((128, 2112, 7168), False, 1520), ((64, 1040, 4096), True, 1521)):
+        assert dg.get_workspace_size(m, n, k) > 0  # K is split: the call uses the scratch
+        out = "fp32" if with_c else "bf16"
+        x = gen_dense(m, n, k, seed=seed, with_c=with_c, out_dtype=out)
+        c = c_tensor(x["c"], out) if with_c else None
+        want = out_buffer((m,), n, out)
+        _with_workspace(x, want, c)
+        d = out_buffer((m,), n, out)
+        keep, args = _args(x, d, c)
+        calls.append((f"M={m} N={n} K={k}", d, keep, args, raw_bits(want)))
+    other = gen_dense(100, 520, 8192, seed=1522)
+    assert dg.get_workspace_size(100, 520, 8192) > 0
+    other_d = out_buffer((100,), 520, "bf16")
+    other_want = out_buffer((100,), 520, "bf16")
+    _with_workspace(other, other_want)
+    _noalloc(other, other_d)  # the scratch address is looked up on an eager call, not under capture
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for *_, args, _ in calls:
+            _noalloc_launch(args)
+    torch.cuda.synchronize()
+    for r in range(4):
+        _noalloc(other, other_d)  # eager, same scratch, another tile grid and split count
+        assert np.array_equal(raw_bits(other_d), raw_bits(other_want)), f"eager call before replay {r}"
+        for _, d, _, _, _ in calls:
+            if d.dtype == torch.bfloat16:
+                d.view(torch.int16).fill_(SENT_BF16)
+            else:
+                d.view(torch.int32).fill_(SENT_F32)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        for name, d, _, _, want in calls:
+            assert np.array_equal(raw_bits(d), want), f"replay {r}: {name} differs from dg_fp8_gemm_nt"
+        note(f"noalloc graph replay {r}: both captured calls bit-identical")
