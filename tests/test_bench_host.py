@@ -106,3 +106,39 @@ def test_counter_summary_derives_clock_and_busy(tmp_path):
     assert "SQ_VALU_MFMA_BUSY_CYCLES per algorithmic MFMA: 32.00" in text
     assert "dispatch duration: 1.90 GHz" in text
     assert "SIMDs): 0.500" in text
+
+
+def _last_json_line(path):
+    with open(path) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def test_committed_bench_lines_keep_the_output_contract():
+    """Every committed bench line carries the fields the JSON contract names, with a
+    roofline object whose fraction follows from its own numbers; the default line also
+    carries the CPU-oracle baseline and a measured traffic figure."""
+    import glob
+
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
+    assert any(p.endswith("bench_baseline.json") for p in paths)
+    for p in paths:
+        d = _last_json_line(p)
+        name = os.path.basename(p)
+        for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                    "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+            assert key in d, (name, key)
+        assert d["n_gpus"] == 1 and d["higher_is_better"] is True and d["scaling"] == "weak", name
+        assert d["vs_baseline"] is None and d["value"] > 0 and d["ms_per_step"] > 0, name
+        assert "workload" in d["config"] and "model" not in d["config"], name
+        r = d["roofline"]
+        assert r["bound"] in ("mfma", "hbm") and r["unit"] == ("TFLOP/s" if r["bound"] == "mfma" else "GB/s"), name
+        assert r["peak"] == (5000.0 if r["bound"] == "mfma" else 8000.0), name
+        assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9 and 0 < r["frac"] < 1, name
+        assert r["traffic"] is None or r["traffic"] > 0, name
+        cpu = d["cpu_baseline"]
+        if cpu is not None:
+            assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0 and cpu["sample"], name
+    base = _last_json_line(os.path.join(ROOT, "profiles", "bench_baseline.json"))
+    assert base["config"]["workload"] == "baseline" and base["cpu_baseline"] is not None
+    assert base["roofline"]["traffic"] is not None
+    assert base["steps"] == 5 and base["warmup"] == 2  # the defaults the driver runs
