@@ -402,7 +402,7 @@ class Case:
 
 class _VendorFp8:
     """The platform's FP8 GEMM on a dense case's operands (per-tensor unit scales,
-    BF16 out): the same MFMA work without the per-slab block-scale promotion."""
+    BF16 out): the same product of the E4M3 codes, without any block scaling."""
 
     def __init__(self, x: dict, dev: str):
         import numpy as np
