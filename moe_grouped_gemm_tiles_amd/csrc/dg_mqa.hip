@@ -15,20 +15,22 @@
 //
 // Mapping: head_dim D = 128 is exactly one K slab of v_mfma_f32_16x16x128_f8f6f4,
 // so one MFMA gives the dot products of 16 heads of one query with 16 keys.
-//   * A workgroup (4 waves) owns a tile of 128 keys and 32 queries.  The kv
-//     tile (16 KiB) is staged once in LDS with direct global->LDS loads, rows
-//     XOR-swizzled like the GEMM's, and every wave keeps all 8 key fragments
-//     in registers.
+//   * A workgroup (4 waves) owns a tile of 256 keys and 32 queries.  The kv
+//     tile (32 KiB) is staged once in LDS with direct global->LDS loads, rows
+//     XOR-swizzled like the GEMM's.  Every query re-reads its q rows from
+//     global memory once per key tile, so the wider the tile the less q
+//     traffic; 256 keys keep the kernel at three waves per SIMD.
 //   * Each wave streams its 8 queries: 4 head fragments of q straight from
 //     global memory (the next query's are loaded while the current one is
-//     computed), 32 MFMAs, and per MFMA output value one integer max (the
-//     ReLU) and one FMA with the head weight, issued three MFMAs behind.
-//     q is the MFMA's first operand, so a lane holds four heads of one key
-//     and the head sum is four FMAs per lane plus two lane swaps
-//     (v_permlane32_swap, v_permlane16_swap) and adds per key.
+//     computed), then key fragment by key fragment (read from LDS one
+//     fragment ahead) 4 MFMAs, one per head fragment, and per MFMA output
+//     value one integer max (the ReLU) and one FMA with the head weight,
+//     issued three MFMAs behind.  q is the MFMA's first operand, so a lane
+//     holds four heads of one key and the head sum is four FMAs per lane plus
+//     two lane swaps (v_permlane32_swap, v_permlane16_swap) and adds per key.
 //   * Two FP32 VALU operations per (query, head, key) against 256 MFMA flops
 //     put the VALU and the matrix core at about the same peak rate on this
-//     chip, so the kernel is bound by both.
+//     chip, so the kernel is bound by both once q traffic is amortised.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -45,7 +47,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kKeys = 128;     // keys per workgroup tile
+constexpr int kKeys = 256;     // keys per workgroup tile
+constexpr int kHalves = kKeys / 128;  // 8 key fragments per head-sum scatter
 constexpr int kQueries = 32;   // queries per workgroup
 constexpr int kWaves = 4;
 constexpr int kD = 128;        // head dim = one MFMA K slab
@@ -64,9 +67,10 @@ struct Params {
   int clean;
 };
 
-// Head sum of the 8 per-key partial sums of a lane across the four lane
-// groups (each group holds 4 of every 16 heads), scattered so that lane group
-// g ends with the sums of keys 2g and 2g+1 of the tile -- the two it stores.
+// Head sum of 8 per-key-fragment partial sums of a lane (one 128-key half of
+// the tile) across the four lane groups (each group holds 4 of every 16
+// heads), scattered so that lane group g ends with the sums of key fragments
+// 2g and 2g+1 of that half -- the two it stores.
 // v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) by 32-lane
 // halves and v_permlane16_swap the same by 16-lane rows (checked on gfx950),
 // so one swap and one add fold two values at once; six swaps and six adds in
@@ -125,7 +129,6 @@ __global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
   }
   any = __syncthreads_or(any);
 
-  i32x8 kvf[kKeys / 16];
   if (any) {
     // kv tile -> LDS: 16 direct 1 KiB loads, 4 per wave; row r's 16-byte chunk
     // c lands at chunk c ^ (r & 7) (the global address is permuted instead).
@@ -142,21 +145,21 @@ __global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
     }
     __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));  // vmcnt(0)
     __syncthreads();
-    const int sw0 = (q4 ^ (r16 & 7)) << 4, sw1 = ((q4 + 4) ^ (r16 & 7)) << 4;
-#pragma unroll
-    for (int kt = 0; kt < kKeys / 16; ++kt) {
-      const uint8_t* row = kv_lds + (kt * 16 + r16) * kD;
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(row + sw0);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(row + sw1);
-      kvf[kt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
   }
+  // key fragment kt of the tile from LDS (lane: key kt*16 + r16, K chunks q4 and q4 + 4)
+  const int sw0 = (q4 ^ (r16 & 7)) << 4, sw1 = ((q4 + 4) ^ (r16 & 7)) << 4;
+  auto read_kv = [&](int kt) {
+    const uint8_t* row = kv_lds + (kt * 16 + r16) * kD;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(row + sw0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(row + sw1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
 
-  // this lane stores keys of fragments 2*q4 and 2*q4+1; their scales
-  float sfl[2];
+  // in each 128-key half this lane stores the keys of fragments 2*q4 and 2*q4+1; their scales
+  float sfl[2 * kHalves];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int key = key0 + (2 * q4 + u) * 16 + r16;
+  for (int u = 0; u < 2 * kHalves; ++u) {
+    const int key = key0 + (u >> 1) * 128 + (2 * q4 + (u & 1)) * 16 + r16;
     sfl[u] = key < p.s_kv ? p.sf[key] : 0.f;
   }
 
@@ -192,34 +195,51 @@ __global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
     const int hi = min(max(load_uniform_i32(p.ke + i), 0), p.s_kv);
     const bool live = any && lo < hi && lo < key0 + kKeys && hi > key0;
     load_q(min(i + kWaves, p.s - 1), qn, wn);
-    float sums[2] = {0.f, 0.f};
+    float sums[2 * kHalves] = {};
     if (live) {
       float acc[kKeys / 16];
 #pragma unroll
       for (int kt = 0; kt < kKeys / 16; ++kt) acc[kt] = 0.f;
-      // Flat sequence of the HT * 8 MFMAs (head fragment t = s / 8, key
-      // fragment kt = s % 8); the ReLU and weight FMAs of MFMA s - (RING - 1)
-      // are issued after MFMA s, so they run under the matrix core.
+      // Flat sequence of the HT * (kKeys / 16) MFMAs (key fragment kt = s / HT,
+      // head fragment t = s % HT): each key fragment is read from LDS once per
+      // query, one fragment ahead, into two register sets.  The ReLU and
+      // weight FMAs of MFMA s - (RING - 1) are issued after MFMA s, so they
+      // run under the matrix core; every acc[kt] still takes its heads in
+      // the order t = 0, 1, ...
       constexpr int T = HT * (kKeys / 16);
       constexpr int RING = 4;
       f32x4 part[RING];
+      i32x8 kf[2];
+      kf[0] = read_kv(0);
 #pragma unroll
       for (int st = 0; st < T + RING - 1; ++st) {
-        if (st < T) part[st % RING] = mfma(qc[st / (kKeys / 16)], kvf[st % (kKeys / 16)]);
+        if (st < T) {
+          const int kt = st / HT, t = st % HT;
+          if (t == 0 && kt + 1 < kKeys / 16) kf[(kt + 1) & 1] = read_kv(kt + 1);
+          part[st % RING] = mfma(qc[t], kf[kt & 1]);
+        }
         const int v = st - (RING - 1);
         if (v >= 0) {
-          const int t = v / (kKeys / 16), kt = v % (kKeys / 16);
+          const int kt = v / HT, t = v % HT;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[kt] = __builtin_fmaf(relu(part[v % RING][r]), wc[t][r], acc[kt]);
         }
       }
-      head_sum_scatter(acc, sums);
+#pragma unroll
+      for (int h = 0; h < kHalves; ++h) {
+        float a8[8], s2[2];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a8[k] = acc[8 * h + k];
+        head_sum_scatter(a8, s2);
+        sums[2 * h] = s2[0];
+        sums[2 * h + 1] = s2[1];
+      }
     }
     if (!live && !p.clean) return;
     float* orow = p.out + (int64_t)i * p.ld_out;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = key0 + (2 * q4 + u) * 16 + r16;
+    for (int u = 0; u < 2 * kHalves; ++u) {
+      const int key = key0 + (u >> 1) * 128 + (2 * q4 + (u & 1)) * 16 + r16;
       if (key >= p.s_kv) continue;
       if (live && key >= lo && key < hi) {
         orow[key] = sums[u] * sfl[u];

@@ -53,6 +53,15 @@ def test_mqa_head_counts(h):
     _check(x, _run(x, True), True, what=f"mqa H={h}")
 
 
+@pytest.mark.parametrize("s_kv", [200, 100, 129])
+def test_mqa_one_partial_key_tile(s_kv):
+    """Fewer keys than one workgroup tile: its later key fragments hold rows past S_kv
+    (loaded as zeros, never stored), with and without -inf cleaning."""
+    x = gen_mqa(33, s_kv, 64, 128, seed=175 + s_kv, ranges="random")
+    for clean in (True, False):
+        _check(x, _run(x, clean), clean, what=f"mqa S_kv={s_kv} clean={clean}")
+
+
 def test_mqa_causal_prefill():
     x = gen_mqa(512, 1024, 64, 128, seed=180, ranges="causal")
     _check(x, _run(x, True), True, what="mqa causal S=512 S_kv=1024")
