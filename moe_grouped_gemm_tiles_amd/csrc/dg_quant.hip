@@ -88,12 +88,44 @@ __device__ __forceinline__ void load8(const void* p, float v[8]) {
   }
 }
 
+// The correctly rounded FP32 division x / s is the fused multiply-add sequence
+// of the IEEE division (reciprocal estimate, one refinement, quotient, two
+// corrections), wrapped in range scaling that only acts when the divisor is
+// denormal or above 2^126, the quotient is denormal, the numerator is below
+// 2^-104 or the operands' exponents are 96 or more apart.  For a divisor in
+// [2^-80, 2^100] and |x| <= 448 s (x from the divisor's own block) none of
+// that applies to a quotient of 2^-10 or more, so there the bare sequence gives
+// the same quotient, and its reciprocal part -- which depends on s alone -- is
+// done once for the eight values.  Smaller quotients round to an E4M3 zero
+// either way; the sign of x is put back so that -0 and negative underflows
+// still give the negative zero code.
+__device__ __forceinline__ bool plain_div_range(float s) { return s >= 0x1p-80f && s <= 0x1p100f; }
+__device__ __forceinline__ float refined_recip(float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+}
+__device__ __forceinline__ float div_by(float x, float s, float y) {
+  const float q0 = x * y;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-s, q0, x), y, q0);
+  const float q2 = __builtin_fmaf(__builtin_fmaf(-s, q1, x), y, q1);
+  return __builtin_copysignf(q2, x);
+}
+
 // Quantize eight values with scale s (FP32 path: correctly rounded x / s).
 template <bool UE8M0>
 __device__ __forceinline__ uint2 quant8(const float v[8], float s) {
   float y[8];
+  if (UE8M0) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = UE8M0 ? v[i] * (1.0f / s) : v[i] / s;  // 1/s is exact for a power of two
+    for (int i = 0; i < 8; ++i) y[i] = v[i] * (1.0f / s);  // 1/s is exact for a power of two
+  } else if (plain_div_range(s)) {
+    const float r = refined_recip(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = div_by(v[i], s, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = v[i] / s;
+  }
   return make_uint2(pack4(y[0], y[1], y[2], y[3]), pack4(y[4], y[5], y[6], y[7]));
 }
 
@@ -149,10 +181,12 @@ __global__ void __launch_bounds__(256) per_token_kernel(const uint8_t* __restric
   }
 }
 
+// (held to 96 registers, five waves per SIMD: the division's per-block reciprocal
+// would otherwise tip the FP32-scale variant to four)
 template <bool BF16_IN, bool UE8M0>
-__global__ void __launch_bounds__(256) per_block_kernel(const uint8_t* __restrict__ w, int64_t ldw_bytes,
-                                                        uint8_t* __restrict__ qo, int64_t ldq, void* __restrict__ sf,
-                                                        int n, int k) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
+per_block_kernel(const uint8_t* __restrict__ w, int64_t ldw_bytes, uint8_t* __restrict__ qo, int64_t ldq,
+                 void* __restrict__ sf, int n, int k) {
   __shared__ float s_amax[4];
   constexpr int ES = BF16_IN ? 2 : 4;
   const int tid = threadIdx.x, rg = tid >> 4, l = tid & 15;

@@ -103,6 +103,50 @@ def test_per_block_bit_exact(dtype, ue):
     assert np.array_equal(sf.view(np.int32), want_sf.view(np.int32))
 
 
+def _extreme_rows(dtype, seed):
+    """Rows of N(0,1) values times 2^k, k from denormal inputs to near the FP32 limit and on
+    both sides of where the FP32 scale amax/448 leaves [2^-80, 2^100]; in every row some
+    values 2^-40 smaller (their quotients round to an E4M3 zero), two -0 and one +0."""
+    rng = np.random.default_rng(seed)
+    ks = [-133, -120, -100, -75, -74, -73, -72, 0, 100, 105, 106, 107, 108, 124]
+    rows = []
+    for k in ks:
+        for _ in range(2):
+            r = rng.standard_normal(512).astype(np.float64) * 2.0 ** k
+            tiny = rng.random(512) < 0.05
+            r[tiny] *= 2.0 ** -40
+            r[rng.integers(0, 512, 2)] = -0.0
+            r[rng.integers(0, 512)] = 0.0
+            rows.append(r.astype(np.float32))
+    x = np.stack(rows)
+    if dtype == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.isfinite(x).all()
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_magnitudes_bit_exact(dtype):
+    """Scales far from 1 take the division's general path, the others the one with the
+    reciprocal refined per block: both must give the oracle's codes and scales."""
+    x = _extreme_rows(dtype, seed=140)
+    q, sf = _run_token(x, dtype, ue=False)
+    want_q, want_sf = oracle.quant_per_token(x)
+    m = x.shape[0]
+    assert np.array_equal(sf[:, :m].view(np.int32), want_sf[:, :m].view(np.int32))
+    bad = np.argwhere(q != want_q)
+    assert bad.size == 0, f"per-token: {len(bad)} codes differ, first at {bad[:3].tolist()}"
+    # row blocks (x holds two rows per k, in the order of ks): amax at k = -72 (scale just
+    # inside the lower bound), k = -74 (just outside), k = 106 (just inside the upper bound),
+    # then a partial block at k = 124 (outside)
+    w = np.concatenate([np.resize(x[0:14], (128, 512)), np.resize(x[0:10], (128, 512)),
+                        np.resize(x[16:22], (128, 512)), np.resize(x[22:28], (50, 512))])
+    qb, sfb = _run_block(w, dtype, ue=False)
+    want_qb, want_sfb = oracle.quant_per_block(w)
+    assert np.array_equal(sfb.view(np.int32), want_sfb.view(np.int32))
+    assert np.array_equal(qb, want_qb), f"per-block: {int((qb != want_qb).sum())} codes differ"
+
+
 def test_cast_then_gemm_matches_oracle():
     """GPU cast of both operands feeding the GPU GEMM equals the oracle's cast + GEMM."""
     xa = gen_quant_input(256, 1024, seed=140)
