@@ -118,8 +118,19 @@ __global__ void __launch_bounds__(kWaves * 64) logits_kernel(const Params p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int key0 = blockIdx.x * kKeys;
-  const int qry0 = blockIdx.y * kQueries;
+  // Workgroups go to the 8 XCDs round-robin in launch order (x fastest).  When
+  // the query blocks come in multiples of 8, XCD x takes query blocks x, x + 8,
+  // ... with all their key tiles in a row, so a block's q rows are fetched into
+  // one XCD's L2 instead of all eight, and the causal work stays spread evenly.
+  int kt_idx = blockIdx.x, qb_idx = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = lin & 7, slot = lin >> 3;
+    qb_idx = xcd + 8 * (slot / (int)gridDim.x);
+    kt_idx = slot % (int)gridDim.x;
+  }
+  const int key0 = kt_idx * kKeys;
+  const int qry0 = qb_idx * kQueries;
 
   // Does any query of this workgroup see a key of this tile?
   bool any = false;
